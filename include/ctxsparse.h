@@ -1,0 +1,144 @@
+/*
+ * ctxsparse — oracle top-k context-sparse decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libctxsparse.so.  Every pointer argument named "device" is GPU memory; the library
+ * never allocates, frees or synchronises: all work is queued on the caller's HIP stream and the
+ * caller owns every buffer, including the workspace.  Calls return before the GPU work finishes.
+ * No global mutable state is kept, so calls from several host threads are safe as long as they
+ * do not share a workspace while in flight.
+ *
+ * The method follows the pages summarising "Inference Time Context Sparsity: Illusion or
+ * Opportunity?":
+ *   - oracle top-k: exact selection of the k highest-scoring cached tokens, made separately for
+ *     every decode token, query and head (technical summary, section 2, sparsity mechanisms);
+ *   - sparse decode attention: softmax attention over only the selected tokens, so a decode step
+ *     moves O(k d) instead of O(N d) bytes (section 3.C, bandwidth-efficiency bullet);
+ *   - dense decode attention over every cached token as the same-GPU baseline (section 1: the
+ *     linear bandwidth cost of dense decoding).
+ * Split evaluation with a log-sum-exp merge is the tiling-with-online-softmax technique named in
+ * the FlashSFA summary ("Scaling Attention via Feature Sparsity", system implementation).
+ *
+ * Notation.  B requests, T new query tokens per request, Hq query heads, Hkv KV heads,
+ * G = Hq / Hkv, d = head_dim.  L_b = seq_lens[b] is request b's cached length counting its T new
+ * tokens.  Query head hq reads KV head hq / G.  A "row" is one (b, t, hq).  Token t sees the
+ * positions 0 .. L_b - T + t (its "visible" range, of length L_b - T + t + 1).
+ * Scores are s_n = (q . K_n) * sm_scale in float32; sm_scale is normally 1/sqrt(d).
+ */
+#ifndef CTXSPARSE_H_
+#define CTXSPARSE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Any non-OK return means nothing was queued on the stream, except
+ * CS_ERR_HIP, which reports a failed kernel launch (work queued before it may have run). */
+typedef enum {
+  CS_OK = 0,
+  CS_ERR_INVALID_ARG = 1,         /* null pointer, non-positive or inconsistent size */
+  CS_ERR_UNSUPPORTED = 2,         /* valid but not implemented: head_dim other than 64/128, ... */
+  CS_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_workspace_size() figure */
+  CS_ERR_HIP = 4                  /* hipGetLastError() reported a launch failure */
+} cs_status;
+
+/* Problem shape of one decode step (host memory). */
+typedef struct {
+  int32_t batch;        /* B  >= 1 */
+  int32_t q_len;        /* T  >= 1: new tokens per request (multi-token decode when > 1) */
+  int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* d: 64 or 128 */
+} cs_decode_shape;
+
+enum { CS_KV_CONTIGUOUS = 0, CS_KV_PAGED = 1 };
+
+/* KV cache descriptor (host struct, device pointers).  K and V are bf16.
+ *   CS_KV_CONTIGUOUS: k, v are [B, Hkv, max_len, d]; position n of (b, h) is row n.
+ *   CS_KV_PAGED:      k, v are pools [num_pages, Hkv, page_size, d]; logical position n of request
+ *                     b lives in page page_table[b * max_pages + n / page_size], slot
+ *                     n % page_size.  page_size is a power of two in [16, 4096].
+ * max_len is a host-side bound on every seq_lens[b] (for paged caches at most
+ * max_pages * page_size); it sizes grids and workspaces.  Device data is trusted as follows:
+ * seq_lens[b] is clamped to [0, max_len] and page ids to [0, num_pages - 1] inside the kernels, so
+ * bad values give wrong results but never out-of-bounds reads. */
+typedef struct {
+  const void* k;             /* device bf16 */
+  const void* v;             /* device bf16 */
+  int32_t layout;            /* CS_KV_CONTIGUOUS or CS_KV_PAGED */
+  int32_t max_len;           /* >= 1 */
+  int32_t page_size;         /* paged only */
+  int32_t max_pages;         /* paged only: columns of page_table */
+  int32_t num_pages;         /* paged only: pool size */
+  const int32_t* page_table; /* paged only: device int32 [B, max_pages] */
+  const int32_t* seq_lens;   /* device int32 [B]: L_b, each >= T for a meaningful step */
+} cs_kv_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* cs_status_str(cs_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t cs_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * topk_index — oracle top-k indexer (a1 score + a2 select).
+ *
+ * For every row (b, t, hq) with k' = min(k_b, visible), writes the k' visible positions with the
+ * largest float32 scores s_n = (q[b,t,hq] . K[b, hq/G, n]) * sm_scale, the lower position first
+ * among equal scores (-0.0 equals +0.0), in ascending position order, then -1 up to k_max.
+ *
+ *   q          device bf16 [B, T, Hq, d]
+ *   k_per_req  device int32 [B] (k_b, clamped to [0, k_max]) or NULL: every request uses k_max
+ *   k_max      1 <= k_max <= max_len; row stride of `indices`
+ *   indices    device int32 [B, T, Hq, k_max] (written)
+ *   workspace  device scratch of at least topk_index_workspace_size() bytes, 256-byte aligned
+ *   stream     hipStream_t (NULL: the default stream)
+ * Errors: CS_ERR_INVALID_ARG for null pointers / bad sizes / non-finite sm_scale,
+ * CS_ERR_UNSUPPORTED for head_dim not in {64, 128} or G * T > 64, CS_ERR_WORKSPACE_TOO_SMALL.
+ * ------------------------------------------------------------------------------------------ */
+size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max);
+cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_decode_attn — attention over index lists (a3 split partials + a4 log-sum-exp combine).
+ *
+ * For every row, over the entries I of indices[b, t, hq, 0:k_max]: entries outside the row's
+ * visible range (in particular -1 padding) are skipped; every other entry counts once per
+ * occurrence, in any order.  With s_i as above, m = max s_i:
+ *   out[b,t,hq,:] = sum_i e^{s_i - m} V[b, hq/G, i, :] / sum_i e^{s_i - m}
+ *   lse[b,t,hq]   = m + ln sum_i e^{s_i - m}          (natural log, scaled-score units)
+ * A row with no valid entry gets out = 0 and lse = -inf.
+ *
+ *   indices     device int32 [B, T, Hq, k_max]
+ *   num_splits  pieces each row's list is cut into (partials merged by log-sum-exp);
+ *               0 picks a value from the shape and the GPU's compute-unit count
+ *   out         device float32 [B, T, Hq, d];  lse: device float32 [B, T, Hq]
+ * The workspace size depends on num_splits; pass the same value to both calls.
+ * ------------------------------------------------------------------------------------------ */
+size_t sparse_decode_attn_workspace_size(const cs_decode_shape* shape, int32_t k_max,
+                                         int32_t num_splits);
+cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             const int32_t* indices, int32_t k_max, float sm_scale,
+                             int32_t num_splits, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * dense_decode_attn — the same-GPU dense baseline (a5): sparse_decode_attn with every visible
+ * position selected, computed by streaming each (b, KV head)'s cache once for all G * T rows.
+ * num_splits: pieces the sequence axis is cut into (0: automatic).
+ * ------------------------------------------------------------------------------------------ */
+size_t dense_decode_attn_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                        int32_t num_splits);
+cs_status dense_decode_attn(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            float sm_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CTXSPARSE_H_ */

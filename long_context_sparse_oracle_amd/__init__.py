@@ -1,0 +1,36 @@
+"""Oracle top-k context-sparse decode attention on AMD Instinct MI355X (gfx950).
+
+The computation lives in libctxsparse.so (hand-written HIP kernels behind the C ABI of
+include/ctxsparse.h); this package is a thin ctypes binding with the same entry-point names:
+
+    topk_index(q, cache, k)                 -> int32 [B, T, Hq, k] selected positions
+    sparse_decode_attn(q, cache, indices)   -> (out fp32 [B, T, Hq, d], lse fp32 [B, T, Hq])
+    dense_decode_attn(q, cache)             -> (out, lse) over every visible position
+    KVCache(k, v, seq_lens, page_table=...) -> contiguous or paged bf16 cache description
+
+Build the library with `python -m long_context_sparse_oracle_amd.build`.  Accessing any of the
+names above without the built library raises ImportError: there is no CPU fallback.
+"""
+
+_BINDING_NAMES = (
+    "KVCache",
+    "CtxSparseError",
+    "topk_index",
+    "topk_index_workspace_size",
+    "sparse_decode_attn",
+    "sparse_decode_attn_workspace_size",
+    "dense_decode_attn",
+    "dense_decode_attn_workspace_size",
+    "LIB",
+    "LIB_PATH",
+)
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import _lib
+
+        return getattr(_lib, name)
+    raise AttributeError(name)

@@ -1,0 +1,321 @@
+// C ABI of libctxsparse.so: argument validation, workspace layout and launch sizing.  Every
+// entry point validates on the host before touching the GPU and queues its kernels on the
+// caller's stream without synchronising or allocating.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ctxsparse.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxGT = 64;             // query rows per KV head (G * T): four 16-row MFMA tiles
+constexpr int kTopkMaxLen = 262144;    // select kernel keeps two position bitmaps in LDS
+constexpr int kMaxDevices = 64;
+constexpr size_t kAlign = 256;
+
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute-unit count of the current device (an immutable property, cached per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+cs_status check_shape(const cs_decode_shape* s) {
+  if (!s) return CS_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->q_len < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return CS_ERR_INVALID_ARG;
+  if (s->num_q_heads % s->num_kv_heads) return CS_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return CS_ERR_UNSUPPORTED;
+  const int64_t gt = (int64_t)(s->num_q_heads / s->num_kv_heads) * s->q_len;
+  if (gt > kMaxGT) return CS_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->num_kv_heads > 65535) return CS_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->q_len * s->num_q_heads > (int64_t)INT32_MAX / 4096)
+    return CS_ERR_UNSUPPORTED;
+  return CS_OK;
+}
+
+cs_status check_kv(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  if (!kv) return CS_ERR_INVALID_ARG;
+  if (!kv->k || !kv->v || !kv->seq_lens) return CS_ERR_INVALID_ARG;
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16) || !aligned(kv->seq_lens, 4))
+    return CS_ERR_INVALID_ARG;
+  if (kv->max_len < 1 || kv->max_len < s->q_len) return CS_ERR_INVALID_ARG;
+  if (kv->layout == CS_KV_CONTIGUOUS) return CS_OK;
+  if (kv->layout != CS_KV_PAGED) return CS_ERR_INVALID_ARG;
+  if (kv->page_size < 1 || kv->max_pages < 1 || kv->num_pages < 1 || !kv->page_table)
+    return CS_ERR_INVALID_ARG;
+  if (!is_pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 4096)
+    return CS_ERR_UNSUPPORTED;
+  if ((int64_t)kv->max_len > (int64_t)kv->max_pages * kv->page_size) return CS_ERR_INVALID_ARG;
+  if (!aligned(kv->page_table, 4)) return CS_ERR_INVALID_ARG;
+  return CS_OK;
+}
+
+cs::KVArgs make_kv(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  cs::KVArgs a;
+  a.k = static_cast<const uint16_t*>(kv->k);
+  a.v = static_cast<const uint16_t*>(kv->v);
+  a.seq_lens = kv->seq_lens;
+  a.max_len = kv->max_len;
+  a.num_kv_heads = s->num_kv_heads;
+  if (kv->layout == CS_KV_PAGED) {
+    a.page_table = kv->page_table;
+    a.page_shift = ilog2(kv->page_size);
+    a.max_pages = kv->max_pages;
+    a.num_pages = kv->num_pages;
+  } else {
+    a.page_table = nullptr;
+    a.page_shift = 0;
+    a.max_pages = 0;
+    a.num_pages = 0;
+  }
+  return a;
+}
+
+int64_t rows_of(const cs_decode_shape* s) {
+  return (int64_t)s->batch * s->q_len * s->num_q_heads;
+}
+int gt_of(const cs_decode_shape* s) { return (s->num_q_heads / s->num_kv_heads) * s->q_len; }
+
+// ---- indexer sizing
+void topk_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, int* chunks) {
+  const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
+  const int64_t target = 4LL * cu_count();
+  int64_t c = ceil_div(groups * kv->max_len, target);
+  c = ceil_div(c, 64) * 64;
+  if (c < 1024) c = 1024;
+  if (c > 16384) c = 16384;
+  *chunk = (int)c;
+  *chunks = (int)ceil_div(kv->max_len, c);
+}
+
+size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  const size_t rows = (size_t)rows_of(s);
+  return align_up(rows * (size_t)kv->max_len * sizeof(float)) + align_up(rows * 4096 * sizeof(uint32_t));
+}
+
+// ---- attention sizing
+int sparse_splits(const cs_decode_shape* s, int k_max, int requested) {
+  int64_t S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    const int64_t rows = rows_of(s);
+    S = ceil_div(4LL * cu_count(), rows);
+    const int64_t by_len = ceil_div(k_max, 64);
+    if (S > by_len) S = by_len;
+  }
+  if (S > k_max) S = k_max;
+  if (S > 256) S = 256;
+  if (S < 1) S = 1;
+  // normalise so every split is non-empty
+  const int64_t chunk = ceil_div(k_max, S);
+  return (int)ceil_div(k_max, chunk);
+}
+
+int dense_splits(const cs_decode_shape* s, const cs_kv_desc* kv, int requested, int* chunk_out) {
+  int64_t S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
+    S = ceil_div(4LL * cu_count(), groups);
+    const int64_t by_len = ceil_div(kv->max_len, 256);
+    if (S > by_len) S = by_len;
+  }
+  if (S > 1024) S = 1024;
+  if (S < 1) S = 1;
+  int64_t chunk = ceil_div(ceil_div(kv->max_len, S), 64) * 64;
+  S = ceil_div(kv->max_len, chunk);
+  *chunk_out = (int)chunk;
+  return (int)S;
+}
+
+size_t attn_ws(const cs_decode_shape* s, int S) {
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)rows_of(s);
+  return align_up(rows * S * (size_t)s->head_dim * sizeof(float)) + align_up(rows * S * 2 * sizeof(float));
+}
+
+cs_status check_ws(void* ws, size_t bytes, size_t need) {
+  if (need == 0) return CS_OK;
+  if (!ws || !aligned(ws, 16)) return CS_ERR_INVALID_ARG;
+  if (bytes < need) return CS_ERR_WORKSPACE_TOO_SMALL;
+  return CS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cs_status_str(cs_status s) {
+  switch (s) {
+    case CS_OK: return "CS_OK";
+    case CS_ERR_INVALID_ARG: return "CS_ERR_INVALID_ARG";
+    case CS_ERR_UNSUPPORTED: return "CS_ERR_UNSUPPORTED";
+    case CS_ERR_WORKSPACE_TOO_SMALL: return "CS_ERR_WORKSPACE_TOO_SMALL";
+    case CS_ERR_HIP: return "CS_ERR_HIP";
+  }
+  return "CS_ERR_UNKNOWN";
+}
+
+int32_t cs_version(void) { return 100; }
+
+size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max) {
+  (void)k_max;
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK) return 0;
+  return topk_ws(shape, kv);
+}
+
+cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !indices || !aligned(q, 16) || !aligned(indices, 4)) return CS_ERR_INVALID_ARG;
+  if (k_per_req && !aligned(k_per_req, 4)) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len) return CS_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
+  const size_t need = topk_ws(shape, kv);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
+
+  cs::TopkLaunch a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = make_kv(shape, kv);
+  a.B = shape->batch;
+  a.T = shape->q_len;
+  a.Hq = shape->num_q_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.GT = gt_of(shape);
+  a.D = shape->head_dim;
+  a.rows = (int)rows_of(shape);
+  a.paged = kv->layout == CS_KV_PAGED;
+  a.scale = sm_scale;
+  a.k_per_req = k_per_req;
+  a.k_max = k_max;
+  topk_chunking(shape, kv, &a.chunk, &a.chunks);
+  char* ws = static_cast<char*>(workspace);
+  a.scores = reinterpret_cast<float*>(ws);
+  a.hist = reinterpret_cast<uint32_t*>(ws + align_up((size_t)a.rows * kv->max_len * sizeof(float)));
+  a.indices = indices;
+  hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+size_t sparse_decode_attn_workspace_size(const cs_decode_shape* shape, int32_t k_max,
+                                         int32_t num_splits) {
+  if (check_shape(shape) != CS_OK || k_max < 1 || num_splits < 0) return 0;
+  return attn_ws(shape, sparse_splits(shape, k_max, num_splits));
+}
+
+cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             const int32_t* indices, int32_t k_max, float sm_scale,
+                             int32_t num_splits, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !indices || !out || !lse) return CS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || num_splits < 0 || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  const int S = sparse_splits(shape, k_max, num_splits);
+  const size_t need = attn_ws(shape, S);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
+
+  cs::AttnLaunch a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = make_kv(shape, kv);
+  a.B = shape->batch;
+  a.T = shape->q_len;
+  a.Hq = shape->num_q_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.GT = gt_of(shape);
+  a.D = shape->head_dim;
+  a.rows = (int)rows_of(shape);
+  a.paged = kv->layout == CS_KV_PAGED;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.indices = indices;
+  a.k_max = k_max;
+  a.S = S;
+  a.chunk = (int)ceil_div(k_max, S);
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
+                    : nullptr;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = cs::launch_sparse(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+size_t dense_decode_attn_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                        int32_t num_splits) {
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK || num_splits < 0) return 0;
+  int chunk;
+  return attn_ws(shape, dense_splits(shape, kv, num_splits, &chunk));
+}
+
+cs_status dense_decode_attn(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            float sm_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !out || !lse || !aligned(q, 16) || !aligned(out, 4) || !aligned(lse, 4))
+    return CS_ERR_INVALID_ARG;
+  if (num_splits < 0 || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  int chunk;
+  const int S = dense_splits(shape, kv, num_splits, &chunk);
+  const size_t need = attn_ws(shape, S);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
+
+  cs::AttnLaunch a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = make_kv(shape, kv);
+  a.B = shape->batch;
+  a.T = shape->q_len;
+  a.Hq = shape->num_q_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.GT = gt_of(shape);
+  a.D = shape->head_dim;
+  a.rows = (int)rows_of(shape);
+  a.paged = kv->layout == CS_KV_PAGED;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.indices = nullptr;
+  a.k_max = 0;
+  a.S = S;
+  a.chunk = chunk;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
+                    : nullptr;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = cs::launch_dense(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal launch descriptors shared by the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace cs {
+
+struct TopkLaunch {
+  const uint16_t* q;
+  KVArgs kv;
+  int B, T, Hq, G, GT, D, rows;
+  bool paged;
+  float scale;
+  const int32_t* k_per_req;
+  int k_max;
+  int chunk, chunks;
+  float* scores;    // [rows, max_len]
+  uint32_t* hist;   // [rows, 4096]
+  int32_t* indices; // [rows, k_max]
+};
+
+struct AttnLaunch {
+  const uint16_t* q;
+  KVArgs kv;
+  int B, T, Hq, G, GT, D, rows;
+  bool paged;
+  float scale_log2;
+  const int32_t* indices;  // sparse only
+  int k_max;               // sparse only
+  int S, chunk;
+  float* part_o;   // [rows, S, D]
+  float* part_ml;  // [rows, S, 2]
+  float* out;
+  float* lse;
+};
+
+size_t select_lds_bytes(int max_len);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+hipError_t launch_sparse(const AttnLaunch& a, hipStream_t stream);
+hipError_t launch_dense(const AttnLaunch& a, hipStream_t stream);
+
+}  // namespace cs

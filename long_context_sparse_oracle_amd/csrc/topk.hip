@@ -1,0 +1,460 @@
+// Oracle top-k indexer for gfx950: a streaming score kernel (q.K^T on MFMA, fused 12-bit
+// radix histogram) and a per-row select kernel (LDS radix refinement, ballot compaction).
+//
+// Method: exact top-k selection of cached tokens per (request, token, query head), as used by the
+// oracle indexer of "Inference Time Context Sparsity: Illusion or Opportunity?" (technical
+// summary, section 2, sparsity mechanisms).  Ranking is by the float32 score
+// s = (q . K) * sm_scale, larger first, lower position first among equal scores.
+#include "device_common.h"
+#include "launch.h"
+
+namespace cs {
+
+constexpr int kHistBins = 4096;      // 12 leading bits of the ordered key
+constexpr int kScoreThreads = 256;   // 4 waves
+constexpr int kScoreUnroll = 2;      // 16-position tiles in flight per wave
+constexpr int kSelThreads = 1024;    // 16 waves
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kCandCap = 8192;       // threshold-bin candidates held in LDS
+
+// ============================================================================ clear
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = value;
+}
+
+// ============================================================================ score + histogram
+// Grid: (chunks, B * Hkv, ceil(G*T / 16)).  One workgroup streams `chunk` positions of one
+// (request, KV head) and scores them against up to 16 of the G*T query rows that read that head
+// (row r = t * G + g, query head h * G + g).  Per 16-position tile a wave issues D/32
+// v_mfma_f32_16x16x32_bf16: A = the 16 query rows (lane l: row l%16, 8 dims), B = K^T (lane l:
+// position l%16, the same 8 dims), so each K row is read once for all rows of the group.
+// Scores of visible positions go to scores[row][n]; their 12-bit key prefix is counted in an LDS
+// histogram (two 16-bit counters per word) that is added to the global one at the end.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kScoreThreads) void score_hist_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk) {
+  extern __shared__ uint32_t lds_hist[];  // [rows_here][kHistBins / 2]
+  constexpr int KS = D / 32;              // MFMA k-steps per tile
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int mt = blockIdx.z;
+  const int Hkv = kv.num_kv_heads;
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int GT = G * T;
+  const int r0 = mt * 16;
+  const int rows_here = min(16, GT - r0);
+  const int L = seq_len_of(kv, b);
+  const int start = c * chunk;
+  if (start >= L) return;
+  const int end = min(start + chunk, L);
+
+  for (int i = threadIdx.x; i < rows_here * (kHistBins / 2); i += kScoreThreads) lds_hist[i] = 0u;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+
+  // A operand: query row r0 + m, dims j*32 + g4*8 .. +8.
+  bf16x8 a[KS];
+  {
+    const int r = r0 + m;
+    if (r < GT) {
+      const int t = r / G, gi = r - (r / G) * G;
+      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  }
+  // Output rows held by this lane: 4*g4 + i (i = 0..3).
+  int vis[4];
+  float* srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * g4 + i;
+    const int r = r0 + rl;
+    if (rl < rows_here) {
+      const int t = r / G, gi = r - (r / G) * G;
+      vis[i] = L - T + t + 1;
+      srow[i] = scores + ((((int64_t)b * T + t) * Hq + (h * G + gi)) * (int64_t)kv.max_len);
+    } else {
+      vis[i] = 0;
+      srow[i] = scores;
+    }
+  }
+  __syncthreads();
+
+  const uint16_t* kbase = kv.k;
+  for (int n0 = start + wave * 16; n0 < end; n0 += 4 * 16 * kScoreUnroll) {
+    uint4 kb[kScoreUnroll][KS];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tile = n0 + u * 64;
+      if (tile < end) {
+        const int n = min(tile + m, L - 1);
+        const int64_t off = kv_row<D, PAGED>(kv, b, h, n) + g4 * 8;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) kb[u][j] = ld16(kbase + off + j * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tile = n0 + u * 64;
+      if (tile >= end) break;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kb[u][j]),
+                                                      acc, 0, 0, 0);
+      const int n = tile + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (n < vis[i]) {
+          const float s = acc[i] * scale;
+          srow[i][n] = s;
+          const uint32_t bin = ord_key(s) >> 20;
+          atomicAdd(&lds_hist[(4 * g4 + i) * (kHistBins / 2) + (bin >> 1)], 1u << ((bin & 1u) * 16));
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int w = threadIdx.x; w < rows_here * (kHistBins / 2); w += kScoreThreads) {
+    const uint32_t v = lds_hist[w];
+    if (v == 0u) continue;
+    const int rl = w / (kHistBins / 2);
+    const int r = r0 + rl;
+    const int t = r / G, gi = r - (r / G) * G;
+    const int64_t grow = ((int64_t)b * T + t) * Hq + (h * G + gi);
+    uint32_t* hp = hist + grow * kHistBins + 2 * (w - rl * (kHistBins / 2));
+    if (v & 0xffffu) __hip_atomic_fetch_add(hp, v & 0xffffu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >> 16) __hip_atomic_fetch_add(hp + 1, v >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ============================================================================ select
+// Block-wide exclusive prefix sum over kSelThreads values.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      const uint32_t t = wsum[w];
+      wsum[w] = acc;
+      acc += t;
+    }
+    wsum[kSelWaves] = acc;
+  }
+  __syncthreads();
+  const uint32_t r = wsum[wave] + x - v;
+  if (total) *total = wsum[kSelWaves];
+  __syncthreads();
+  return r;
+}
+
+struct SelShared {
+  uint32_t wsum[kSelWaves + 1];
+  uint32_t cand_count;
+  uint32_t thr_bin;    // bin holding the k-th largest key
+  uint32_t thr_above;  // keys in higher bins
+  uint32_t thr_count;  // keys in the threshold bin
+  uint32_t found;
+};
+
+// Finds, over `nbins` counters hist[0..nbins) (bin nbins-1 highest), the bin holding the need-th
+// largest key.  Each thread covers nbins / kSelThreads consecutive bins, highest bins on thread 0.
+// Returns the total count.
+template <int PER>
+__device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t need, SelShared& sh) {
+  uint32_t cnt[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int bin = nbins - 1 - (threadIdx.x * PER + e);
+    cnt[e] = hist[bin];
+    sum += cnt[e];
+  }
+  if (threadIdx.x == 0) sh.found = 0u;
+  uint32_t total;
+  uint32_t above = block_excl_scan(sum, sh.wsum, &total);
+  if (above < need && above + sum >= need) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (above + cnt[e] >= need) {
+        sh.thr_bin = (uint32_t)(nbins - 1 - (threadIdx.x * PER + e));
+        sh.thr_above = above;
+        sh.thr_count = cnt[e];
+        sh.found = 1u;
+        break;
+      }
+      above += cnt[e];
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+// Per row (b, t, hq): select the kk = min(k_b, visible) largest scores.
+//  1. threshold bin T12 of the 12-bit key prefix from the fused histogram (rebuilt from the scores
+//     when it does not add up to the visible count);
+//  2. one pass over the scores: keys above T12 are marked in an LDS bitmap (one ballot per 64
+//     positions), keys in T12 are appended to an LDS candidate list;
+//  3. two 10-bit radix rounds over the candidates give the exact k-th key K* and how many keys
+//     equal to K* are taken (lowest positions first); when T12 holds more than kCandCap keys the
+//     rounds read the scores instead;
+//  4. the bitmap is emitted in ascending position order by a block prefix sum of popcounts.
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_req, int T, int Hq,
+    int max_len, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* hist_s = smem;                      // kHistBins
+  uint32_t* gt_bits = hist_s + kHistBins;       // bitmap_words
+  uint32_t* eq_bits = gt_bits + bitmap_words;   // bitmap_words
+  uint32_t* cand_key = eq_bits + bitmap_words;  // kCandCap
+  uint32_t* cand_pos = cand_key + kCandCap;     // kCandCap
+  __shared__ SelShared sh;
+
+  const int row = blockIdx.x;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > max_len ? max_len : L);
+  const int vis = max(0, L - T + t + 1);
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, vis);
+  int32_t* out = indices + (int64_t)row * k_max;
+  const float* srow = scores + (int64_t)row * max_len;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  if (kk == vis) {  // everything visible is selected (also kk == 0)
+    for (int i = tid; i < k_max; i += kSelThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
+
+  const int words = ((vis + 63) >> 6) * 2;  // bitmap words touched (64-position granules)
+  for (int i = tid; i < words; i += kSelThreads) {
+    gt_bits[i] = 0u;
+    eq_bits[i] = 0u;
+  }
+  if (tid == 0) sh.cand_count = 0u;
+
+  // ---- 1. threshold bin of the 12-bit prefix
+  const uint32_t* hrow = hist + (int64_t)row * kHistBins;
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist_s[i] = hrow[i];
+  __syncthreads();
+  uint32_t total = find_threshold<kHistBins / kSelThreads>(hist_s, kHistBins, (uint32_t)kk, sh);
+  if (total != (uint32_t)vis || !sh.found) {
+    // histogram does not describe this row: rebuild it from the scores
+    for (int i = tid; i < kHistBins; i += kSelThreads) hist_s[i] = 0u;
+    __syncthreads();
+    for (int n = tid; n < vis; n += kSelThreads) atomicAdd(&hist_s[ord_key(srow[n]) >> 20], 1u);
+    __syncthreads();
+    find_threshold<kHistBins / kSelThreads>(hist_s, kHistBins, (uint32_t)kk, sh);
+  }
+  const uint32_t T12 = sh.thr_bin;
+  uint32_t need = (uint32_t)kk - sh.thr_above;  // keys still to take from bin T12
+  const uint32_t cntT = sh.thr_count;
+  const bool fast = cntT <= (uint32_t)kCandCap;
+  __syncthreads();
+
+  // ---- 2. mark keys above T12, collect keys in T12
+  for (int base = wave * 64; base < vis; base += kSelThreads * 2) {
+    float sv[2];
+    int nn[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      nn[u] = base + u * kSelThreads + lane;
+      sv[u] = nn[u] < vis ? srow[nn[u]] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int nb = base + u * kSelThreads;
+      if (nb >= vis) break;
+      const bool valid = nn[u] < vis;
+      const uint32_t key = ord_key(sv[u]);
+      const uint32_t bin = key >> 20;
+      const uint64_t gm = __ballot(valid && bin > T12);
+      if (lane == 0) {
+        gt_bits[nb >> 5] = (uint32_t)gm;
+        gt_bits[(nb >> 5) + 1] = (uint32_t)(gm >> 32);
+      }
+      if (fast) {
+        const bool eq = valid && bin == T12;
+        const uint64_t em = __ballot(eq);
+        if (em) {
+          uint32_t slot0 = 0;
+          if (lane == 0) slot0 = atomicAdd(&sh.cand_count, (uint32_t)__popcll(em));
+          slot0 = __shfl(slot0, 0);
+          const uint32_t slot = slot0 + __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
+          if (eq && slot < (uint32_t)kCandCap) {
+            cand_key[slot] = key;
+            cand_pos[slot] = (uint32_t)nn[u];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. exact threshold key K* inside bin T12 (two 10-bit rounds)
+  uint32_t prefix = T12;  // resolved leading bits
+  uint32_t cnt_eq = 0;
+  for (int round = 0; round < 2; ++round) {
+    const int shift = round == 0 ? 10 : 0;
+    for (int i = tid; i < 1024; i += kSelThreads) hist_s[i] = 0u;
+    __syncthreads();
+    if (fast) {
+      const uint32_t c = min(sh.cand_count, (uint32_t)kCandCap);
+      for (uint32_t i = tid; i < c; i += kSelThreads) {
+        const uint32_t key = cand_key[i];
+        if ((key >> (shift + 10)) == prefix) atomicAdd(&hist_s[(key >> shift) & 1023u], 1u);
+      }
+    } else {
+      for (int n = tid; n < vis; n += kSelThreads) {
+        const uint32_t key = ord_key(srow[n]);
+        if ((key >> (shift + 10)) == prefix) atomicAdd(&hist_s[(key >> shift) & 1023u], 1u);
+      }
+    }
+    __syncthreads();
+    find_threshold<1>(hist_s, 1024, need, sh);
+    prefix = (prefix << 10) | sh.thr_bin;
+    need -= sh.thr_above;
+    cnt_eq = sh.thr_count;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;  // exact key of the kk-th largest score
+  const bool take_all_eq = (cnt_eq == need);
+
+  // mark keys of bin T12 that are > K* (and == K*)
+  if (fast) {
+    const uint32_t c = min(sh.cand_count, (uint32_t)kCandCap);
+    for (uint32_t i = tid; i < c; i += kSelThreads) {
+      const uint32_t key = cand_key[i];
+      const uint32_t p = cand_pos[i];
+      if (key > kstar || (key == kstar && take_all_eq))
+        atomicOr(&gt_bits[p >> 5], 1u << (p & 31));
+      else if (key == kstar)
+        atomicOr(&eq_bits[p >> 5], 1u << (p & 31));
+    }
+  } else {
+    for (int nb = wave * 64; nb < vis; nb += kSelThreads) {
+      const int n = nb + lane;
+      const bool valid = n < vis;
+      const uint32_t key = valid ? ord_key(srow[n]) : 0u;
+      const bool inbin = valid && (key >> 20) == T12;
+      const uint64_t gm = __ballot(inbin && (key > kstar || (key == kstar && take_all_eq)));
+      const uint64_t em = __ballot(inbin && key == kstar && !take_all_eq);
+      if (lane == 0) {
+        gt_bits[nb >> 5] |= (uint32_t)gm;
+        gt_bits[(nb >> 5) + 1] |= (uint32_t)(gm >> 32);
+        eq_bits[nb >> 5] |= (uint32_t)em;
+        eq_bits[(nb >> 5) + 1] |= (uint32_t)(em >> 32);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;  // bitmap words per thread
+  const int w0 = tid * wpt;
+  if (!take_all_eq) {
+    // keep the `need` lowest positions among keys equal to K*
+    uint32_t cnt = 0;
+    for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(eq_bits[w]);
+    uint32_t before = block_excl_scan(cnt, sh.wsum, nullptr);
+    for (int w = w0; w < min(w0 + wpt, words); ++w) {
+      uint32_t bits = eq_bits[w];
+      while (bits) {
+        const uint32_t bit = bits & (0u - bits);
+        if (before < need) gt_bits[w] |= bit;
+        ++before;
+        bits ^= bit;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 4. emit ascending positions
+  uint32_t cnt = 0;
+  for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(gt_bits[w]);
+  uint32_t pos = block_excl_scan(cnt, sh.wsum, nullptr);
+  for (int w = w0; w < min(w0 + wpt, words); ++w) {
+    uint32_t bits = gt_bits[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      if (pos < (uint32_t)k_max) out[pos] = w * 32 + bit;
+      ++pos;
+      bits &= bits - 1;
+    }
+  }
+  for (int i = kk + tid; i < k_max; i += kSelThreads) out[i] = -1;
+}
+
+// ============================================================================ launchers
+size_t select_lds_bytes(int max_len) {
+  const int words = ((max_len + 63) / 64) * 2;
+  return sizeof(uint32_t) * ((size_t)kHistBins + 2 * (size_t)words + 2 * (size_t)kCandCap);
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
+  const int rows_tile = a.GT < 16 ? a.GT : 16;
+  const size_t lds = (size_t)rows_tile * (kHistBins / 2) * sizeof(uint32_t);
+  auto kern = score_hist_kernel<D, PAGED>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(a.chunks, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
+  hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
+                     a.scale, a.scores, a.hist, a.chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
+  hipError_t e = launch_fill_u32(a.hist, (int64_t)a.rows * kHistBins, 0u, stream);
+  if (e != hipSuccess) return e;
+  if (a.D == 128)
+    e = a.paged ? launch_score_t<128, true>(a, stream) : launch_score_t<128, false>(a, stream);
+  else
+    e = a.paged ? launch_score_t<64, true>(a, stream) : launch_score_t<64, false>(a, stream);
+  if (e != hipSuccess) return e;
+  const size_t lds = select_lds_bytes(a.kv.max_len);
+  if (lds > 65536) {
+    e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int words = ((a.kv.max_len + 63) / 64) * 2;
+  hipLaunchKernelGGL(select_kernel, dim3(a.rows), dim3(kSelThreads), lds, stream, a.scores,
+                     a.hist, a.kv.seq_lens, a.k_per_req, a.T, a.Hq, a.kv.max_len, a.k_max, words,
+                     a.indices);
+  return hipGetLastError();
+}
+
+}  // namespace cs
