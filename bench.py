@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark: one oracle-top-k sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama3_8b_n32k_k655]
+
+A step is one pass of the whole hot path over one decode batch, on one stream:
+    flush -> topk_index -> flush -> sparse_decode_attn -> flush -> dense_decode_attn
+`flush` reads a 2 GiB scratch buffer so that neither L2 nor the 256 MB Infinity Cache holds any
+KV bytes when a hot-path call starts (every call is measured from cold caches).  Each call is
+bracketed by HIP events recorded on the stream it runs on.  Inputs are seeded synthetic tensors
+drawn on the GPU before the timed region.
+
+Prints ONE JSON line.  `value` is the sparse decode attention's gathered-KV throughput: the
+distinct K/V rows the step's index lists name (counted once per (request, KV head) group, 512 B
+each at d=128) plus index, query and output bytes, divided by the mean duration of the
+sparse_decode_attn call.  Also reported: µs of every call, speedup over the dense decode on the
+same inputs, a roofline object per kernel and the CPU oracle timed on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode µs/step + gathered-KV GB/s (% HBM peak), speedup vs dense at 50×"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama3_8b_n32k_k655"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "sparse_decode_attn": ["long_context_sparse_oracle_amd/csrc/attention.hip",
+                           "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "dense_decode_attn": ["long_context_sparse_oracle_amd/csrc/attention.hip",
+                          "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "topk_index": ["long_context_sparse_oracle_amd/csrc/topk.hip",
+                   "long_context_sparse_oracle_amd/csrc/device_common.h"],
+}
+
+
+def source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--sweep-k", default=None, help="k for the sweep workload (s10/s50/s100/s1000)")
+    p.add_argument("--sparse-splits", type=int, default=0)
+    p.add_argument("--dense-splits", type=int, default=0)
+    p.add_argument("--no-flush", action="store_true", help="warm caches (not the reported figure)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the CPU oracle leg (0 disables it)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, idx):
+    """Bytes the method must move per call (d-dim bf16 rows, int32 indices, fp32 outputs)."""
+    import torch
+
+    B, T, Hq, Hkv, d = wl.batch, wl.q_len, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    G = Hq // Hkv
+    rows = B * T * Hq
+    row_bytes = d * 2
+    q_bytes = rows * d * 2
+    o_bytes = rows * d * 4 + rows * 4
+    tokens = int(wl.seq_lens.to(torch.int64).sum())
+    # distinct selected rows per (request, KV head) group
+    grp = idx.view(B, T, Hkv, G, -1).permute(0, 2, 1, 3, 4).reshape(B * Hkv, -1).long()
+    mark = torch.zeros((B * Hkv, wl.max_len + 1), dtype=torch.bool, device=idx.device)
+    mark.scatter_(1, torch.where(grp < 0, wl.max_len, grp), True)
+    distinct = int(mark[:, : wl.max_len].sum())
+    nominal = int((idx >= 0).sum())
+    index_bytes = idx.numel() * 4
+    return {
+        "sparse": 2 * distinct * row_bytes + index_bytes + q_bytes + o_bytes,
+        "sparse_nominal": 2 * nominal * row_bytes + index_bytes + q_bytes + o_bytes,
+        "distinct_rows": distinct,
+        "selected_rows": nominal,
+        "dense": 2 * tokens * Hkv * row_bytes + q_bytes + o_bytes,
+        "topk": tokens * Hkv * row_bytes + index_bytes + q_bytes,
+    }
+
+
+def cpu_baseline(wl, gathered_bytes, seconds):
+    """The CPU oracle (top-k + sparse attention per row) timed on the host on a bounded sample
+    of the same workload, scaled to the full step."""
+    import numpy as np
+    import torch
+
+    import oracle  # CPU oracle: benchmark baseline leg only
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    B, T, Hq, Hkv = wl.batch, wl.q_len, wl.num_q_heads, wl.num_kv_heads
+    G = Hq // Hkv
+    groups = [(b, h) for b in range(B) for h in range(Hkv)]
+    order = np.random.default_rng(7).permutation(len(groups))
+    qb = wl.q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    q = oracle.bf16_bits_to_f64(qb)
+    kreq = wl.k_per_req.cpu().numpy()
+    lens = wl.seq_lens.cpu().numpy()
+    done_rows = 0
+    elapsed = 0.0
+    n_groups = 0
+    for gi in order:
+        b, h = groups[gi]
+        L = int(lens[b])
+        if wl.layout == "contiguous":
+            kb = wl.k_cache[b, h, :L].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            vb = wl.v_cache[b, h, :L].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        else:
+            n = torch.arange(L, device=wl.page_table.device)
+            pages = wl.page_table[b, n // wl.page_size].long()
+            kb = wl.k_cache[pages, h, n % wl.page_size].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            vb = wl.v_cache[pages, h, n % wl.page_size].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        K = oracle.bf16_bits_to_f64(kb)
+        V = oracle.bf16_bits_to_f64(vb)
+        for t in range(T):
+            vis = oracle.visible_length(L, T, t)
+            for g in range(G):
+                hq = h * G + g
+                sel = oracle.row_topk(q[b, t, hq], K, vis, int(kreq[b]))
+                oracle.row_sparse(q[b, t, hq], K, V, sel, vis)
+                done_rows += 1
+        elapsed += time.perf_counter() - t0
+        n_groups += 1
+        if elapsed >= seconds:
+            break
+    rows = B * T * Hq
+    step_s = elapsed / done_rows * rows
+    return {
+        "value": round(gathered_bytes / step_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "us_per_step": round(step_s * 1e6, 1),
+        "sample": (
+            f"{done_rows} of {rows} rows ({n_groups} of {len(groups)} (request, KV head) groups): "
+            f"float64 NumPy oracle top-k + sparse attention per row, {elapsed:.1f} s, scaled "
+            f"linearly to the full step" if done_rows < rows else
+            f"all {rows} rows: float64 NumPy oracle top-k + sparse attention, {elapsed:.1f} s"
+        ),
+    }
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode step "
+              f"runs on a single device and has no multi-GPU execution path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_sparse_oracle_amd as cs
+    from workloads import make_named
+    from workloads.synth import SWEEP_K
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    overrides = {}
+    if args.workload == "sweep_b16_n128k" and args.sweep_k:
+        overrides["k"] = SWEEP_K[args.sweep_k]
+    wl = make_named(args.workload, device=dev, **overrides)
+    torch.cuda.synchronize()
+    cache = cs.KVCache(wl.k_cache, wl.v_cache, wl.seq_lens, page_table=wl.page_table,
+                       max_len=wl.max_len)
+    B, T, Hq, d = wl.batch, wl.q_len, wl.num_q_heads, wl.head_dim
+    k_max = wl.k_max
+    kptr = wl.k_per_req
+
+    # buffers allocated once: the timed region allocates nothing
+    indices = torch.empty((B, T, Hq, k_max), dtype=torch.int32, device=dev)
+    out_s = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    out_d = torch.empty_like(out_s)
+    lse_d = torch.empty_like(lse_s)
+    ws_t = torch.empty(max(1, cs.topk_index_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, cs.sparse_decode_attn_workspace_size(wl.q, cache, k_max, args.sparse_splits)),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, cs.dense_decode_attn_workspace_size(wl.q, cache, args.dense_splits)),
+                       dtype=torch.uint8, device=dev)
+    # cache flush by reading 2 GiB: evicts every KV line from L2 and the Infinity Cache and leaves
+    # clean lines behind (a write flush would leave dirty lines whose write-back the next call
+    # would pay for)
+    flush_buf = None if args.no_flush else torch.ones((2 << 30) // 8, dtype=torch.int64, device=dev)
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def flush():
+        if flush_buf is not None:
+            torch.sum(flush_buf, dim=0, out=flush_out)
+
+    calls = {
+        "topk_index": lambda: cs.topk_index(wl.q, cache, kptr, k_max=k_max, indices=indices, workspace=ws_t),
+        "sparse_decode_attn": lambda: cs.sparse_decode_attn(wl.q, cache, indices, num_splits=args.sparse_splits,
+                                                            out=out_s, lse=lse_s, workspace=ws_s),
+        "dense_decode_attn": lambda: cs.dense_decode_attn(wl.q, cache, num_splits=args.dense_splits,
+                                                          out=out_d, lse=lse_d, workspace=ws_d),
+    }
+    times = {k: [] for k in calls}
+
+    def step(record):
+        evs = []
+        for name, fn in calls.items():
+            flush()
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                evs.append((name, e0, e1))
+            else:
+                fn()
+        return evs
+
+    print(f"[bench] workload {args.workload}: B{B} T{T} Hq{Hq} Hkv{wl.num_kv_heads} d{d} "
+          f"max_len {wl.max_len} k_max {k_max} layout {wl.layout}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    all_evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_evs.extend(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for name, e0, e1 in all_evs:
+        times[name].append(e0.elapsed_time(e1) * 1000.0)  # µs
+
+    ab = algorithmic_bytes(wl, indices)
+    mean = {k: statistics.fmean(v) for k, v in times.items()}
+    med = {k: statistics.median(v) for k, v in times.items()}
+    traffic = load_traffic()
+
+    def roofline(name, bytes_per_launch):
+        achieved = bytes_per_launch / (mean[name] * 1e-6) / 1e9
+        tr = traffic.get(args.workload, {}).get(name)
+        tr_val = None
+        if tr and tr.get("source_sha256") == source_hash(name):
+            tr_val = tr.get("bytes_per_launch")
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr_val}
+
+    sparse_gbs = ab["sparse"] / (mean["sparse_decode_attn"] * 1e-6) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(sparse_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": B, "q_len": T, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": d, "context": wl.max_len, "k": k_max, "layout": wl.layout,
+            "sparsity": round(wl.max_len / k_max, 1) if wl.layout == "contiguous" else 50.0,
+            "cold_cache": flush_buf is not None,
+        },
+        "sparse_us": round(mean["sparse_decode_attn"], 2),
+        "sparse_us_median": round(med["sparse_decode_attn"], 2),
+        "topk_us": round(mean["topk_index"], 2),
+        "dense_us": round(mean["dense_decode_attn"], 2),
+        "speedup_vs_dense": round(mean["dense_decode_attn"] / mean["sparse_decode_attn"], 3),
+        "e2e_speedup_vs_dense": round(mean["dense_decode_attn"] / (mean["topk_index"] + mean["sparse_decode_attn"]), 3),
+        "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
+        "kernel_us_per_step": round(sum(mean.values()), 2),
+        "gathered_bytes": ab["sparse"],
+        "distinct_rows": ab["distinct_rows"],
+        "selected_rows": ab["selected_rows"],
+        "roofline": roofline("sparse_decode_attn", ab["sparse"]),
+        "roofline_kernels": {
+            "topk_index": roofline("topk_index", ab["topk"]),
+            "dense_decode_attn": roofline("dense_decode_attn", ab["dense"]),
+        },
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, ab["sparse"], args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
