@@ -15,6 +15,8 @@ distinct K/V rows the step's index lists name (counted once per (request, KV hea
 each at d=128) plus index, query and output bytes, divided by the mean duration of the
 sparse_decode_attn call.  Also reported: µs of every call, speedup over the dense decode on the
 same inputs, a roofline object per kernel and the CPU oracle timed on the host cores.
+Call durations come from HIP events created with hipEventDisableSystemFence; an event pair
+around one call still counts about 4 µs of dispatch latency on top of the kernels' run time.
 """
 
 from __future__ import annotations
@@ -165,6 +167,58 @@ def cpu_baseline(wl, gathered_bytes, seconds):
     }
 
 
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence: recording them skips the system-scope
+    cache writeback/invalidate that default events perform, which would otherwise add about
+    1.6 µs of idle time to every timed call.  Recorded on the stream the library launches on."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        path = None
+        for cand in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+            try:
+                self.hip = ctypes.CDLL(cand)
+                path = cand
+                break
+            except OSError:
+                continue
+        if path is None:
+            raise RuntimeError("libamdhip64 not found")
+        self.ct = ctypes
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        torch.cuda.synchronize()
+
+    def create(self):
+        e = self.ct.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        return e
+
+    def record(self, e, stream_handle):
+        st = self.hip.hipEventRecord(e, self.ct.c_void_p(stream_handle))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_us(self, e0, e1):
+        ms = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(ms), e0, e1)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value * 1000.0
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
 def load_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
@@ -230,16 +284,19 @@ def main():
     }
     times = {k: [] for k in calls}
 
-    def step(record):
+    hev = HipEvents()
+    sh = stream.cuda_stream
+    pool = [(hev.create(), hev.create()) for _ in range(len(calls) * args.steps)]
+
+    def step(record, k=0):
         evs = []
-        for name, fn in calls.items():
+        for j, (name, fn) in enumerate(calls.items()):
             flush()
             if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+                e0, e1 = pool[k * len(calls) + j]
+                hev.record(e0, sh)
                 fn()
-                e1.record(stream)
+                hev.record(e1, sh)
                 evs.append((name, e0, e1))
             else:
                 fn()
@@ -260,12 +317,15 @@ def main():
     all_evs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        all_evs.extend(step(True))
+    for k in range(args.steps):
+        all_evs.extend(step(True, k))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for name, e0, e1 in all_evs:
-        times[name].append(e0.elapsed_time(e1) * 1000.0)  # µs
+        times[name].append(hev.elapsed_us(e0, e1))
+    for e0, e1 in pool:
+        hev.destroy(e0)
+        hev.destroy(e1)
 
     ab = algorithmic_bytes(wl, indices)
     mean = {k: statistics.fmean(v) for k, v in times.items()}
@@ -311,6 +371,8 @@ def main():
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
+        "algorithmic_bytes": {"topk_index": ab["topk"], "sparse_decode_attn": ab["sparse"],
+                              "dense_decode_attn": ab["dense"]},
         "distinct_rows": ab["distinct_rows"],
         "selected_rows": ab["selected_rows"],
         "roofline": roofline("sparse_decode_attn", ab["sparse"]),
