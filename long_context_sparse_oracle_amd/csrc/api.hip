@@ -102,7 +102,7 @@ void topk_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, i
   const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
   const int64_t target = 4LL * cu_count();
   int64_t c = ceil_div(groups * kv->max_len, target);
-  c = ceil_div(c, 64) * 64;
+  c = ceil_div(c, 256) * 256;
   if (c < 1024) c = 1024;
   if (c > 16384) c = 16384;
   *chunk = (int)c;
@@ -115,22 +115,40 @@ size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) {
 }
 
 // ---- attention sizing
-int sparse_splits(const cs_decode_shape* s, int k_max, int requested) {
+// Gather plan.  A wave handles one round of E index entries.  When every wave of the call fits
+// on the GPU at once (12 per CU at E = 64), whole lists go to single workgroups of up to 12
+// waves (no partials to merge).  Larger calls use E = 32 and 4-wave workgroups, several per CU,
+// so load and compute phases of different workgroups overlap.
+struct SparsePlan {
+  int S, chunk, waves, wave_entries;
+};
+
+SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
+  const int64_t rows = rows_of(s);
+  const bool one_generation = rows * ceil_div(k_max, 64) <= 12LL * cu_count();
+  const int E = one_generation ? 64 : 32;
+  const int maxw = one_generation ? 12 : 4;
+  const int64_t waves_needed = ceil_div(k_max, E);
   int64_t S;
   if (requested > 0) {
     S = requested;
   } else {
-    const int64_t rows = rows_of(s);
-    S = ceil_div(4LL * cu_count(), rows);
-    const int64_t by_len = ceil_div(k_max, 64);
-    if (S > by_len) S = by_len;
+    S = ceil_div(waves_needed, maxw);
+    const int64_t spread = ceil_div(cu_count(), rows);
+    const int64_t cap = waves_needed < spread ? waves_needed : spread;
+    if (S < cap) S = cap;
   }
   if (S > k_max) S = k_max;
-  if (S > 256) S = 256;
+  if (S > 1024) S = 1024;
   if (S < 1) S = 1;
-  // normalise so every split is non-empty
-  const int64_t chunk = ceil_div(k_max, S);
-  return (int)ceil_div(k_max, chunk);
+  const int64_t chunk = ceil_div(k_max, S);  // every split non-empty
+  SparsePlan p;
+  p.S = (int)ceil_div(k_max, chunk);
+  p.chunk = (int)chunk;
+  const int64_t w = ceil_div(chunk, E);
+  p.waves = (int)(w > maxw ? maxw : w);
+  p.wave_entries = E;
+  return p;
 }
 
 int dense_splits(const cs_decode_shape* s, const cs_kv_desc* kv, int requested, int* chunk_out) {
@@ -142,6 +160,12 @@ int dense_splits(const cs_decode_shape* s, const cs_kv_desc* kv, int requested, 
     S = ceil_div(4LL * cu_count(), groups);
     const int64_t by_len = ceil_div(kv->max_len, 256);
     if (S > by_len) S = by_len;
+  }
+  if (kv->layout == CS_KV_PAGED) {
+    // a paged chunk's page ids are staged in LDS: keep them within 8192 ids (32 KB)
+    const int64_t max_chunk = (8190LL * kv->page_size) / 64 * 64;
+    const int64_t min_S = ceil_div(kv->max_len, max_chunk);
+    if (S < min_S) S = min_S;
   }
   if (S > 1024) S = 1024;
   if (S < 1) S = 1;
@@ -227,7 +251,7 @@ cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_de
 size_t sparse_decode_attn_workspace_size(const cs_decode_shape* shape, int32_t k_max,
                                          int32_t num_splits) {
   if (check_shape(shape) != CS_OK || k_max < 1 || num_splits < 0) return 0;
-  return attn_ws(shape, sparse_splits(shape, k_max, num_splits));
+  return attn_ws(shape, sparse_plan(shape, k_max, num_splits).S);
 }
 
 cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
@@ -241,7 +265,8 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 4) || !aligned(lse, 4))
     return CS_ERR_INVALID_ARG;
   if (k_max < 1 || num_splits < 0 || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
-  const int S = sparse_splits(shape, k_max, num_splits);
+  const SparsePlan plan = sparse_plan(shape, k_max, num_splits);
+  const int S = plan.S;
   const size_t need = attn_ws(shape, S);
   if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
 
@@ -260,7 +285,9 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   a.indices = indices;
   a.k_max = k_max;
   a.S = S;
-  a.chunk = (int)ceil_div(k_max, S);
+  a.chunk = plan.chunk;
+  a.waves = plan.waves;
+  a.wave_entries = plan.wave_entries;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
@@ -308,6 +335,8 @@ cs_status dense_decode_attn(const cs_decode_shape* shape, const void* q, const c
   a.k_max = 0;
   a.S = S;
   a.chunk = chunk;
+  a.waves = 0;
+  a.wave_entries = 0;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))

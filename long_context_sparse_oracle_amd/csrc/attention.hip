@@ -38,23 +38,36 @@ __device__ __forceinline__ void store_result(float O, float M, float Lsum, int c
 }
 
 // ============================================================================ sparse partial
-// One workgroup per (row, split), rows of one (request, KV head) kept on one XCD: workgroup w runs
-// on XCD w % 8, so group g is given the ids congruent to g mod 8 and rows of a GQA group that pick
-// the same token find its K/V lines in that XCD's L2.
-// Inside a wave, D/8 lanes hold one selected position (8 dims = 16 bytes of K and of V each), so
-// a wave gathers 64/(D/8) whole 256-byte (D=128) rows per step, kUnroll steps in flight.
-template <int D, bool PAGED>
-__global__ __launch_bounds__(kAttnThreads) void sparse_partial_kernel(
+// One workgroup per (row, split): W waves (blockDim.x = 64 W), each gathering kSparseWaveEntries
+// entries of the row's index list per round.  Rows of one (request, KV head) are kept on one XCD
+// (workgroup w runs on XCD w % 8, so group g gets the ids congruent to g mod 8): rows of a GQA
+// group that pick the same token find its K/V lines in that XCD's L2.
+// Per round a wave loads its indices with one coalesced load, hands them to the lanes with
+// ds_bpermute, then issues every K and V load of the round before using any of them: D/8 lanes
+// hold one position (8 dims = 16 bytes of K and of V), 64/(D/8) positions per step, so a round
+// keeps 64 whole rows (32 KB of K and V at D=128) in flight per wave.  Scores are reduced across the D/8
+// lanes with DPP, the round's softmax statistics are merged into the running (m, l, o) and, at
+// the end, the waves' and position groups' states are merged through LDS.
+constexpr int kSparseMaxWaves = 12;
+
+// E = entries per wave round: 64 for calls whose waves all fit on the GPU at once (whole lists
+// in one workgroup of up to 12 waves), 32 for larger calls (4-wave workgroups at >= 5 waves per
+// SIMD, so many rounds of different workgroups overlap).
+template <int D, bool PAGED, int E>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64, E == 64 ? kSparseMaxWaves * 64 : 256),
+                               amdgpu_waves_per_eu(E == 64 ? 3 : 5)))
+sparse_partial_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, const int32_t* __restrict__ indices, int T, int Hq,
     int G, int k_max, float scale_log2, int S, int chunk, int n_groups, int items_per_group,
     float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ out,
     float* __restrict__ lse) {
-  constexpr int LPP = D / 8;        // lanes per position
-  constexpr int PPW = kWave / LPP;  // positions per wave step
-  constexpr int U = 4;              // steps in flight
-  __shared__ float red_m[kAttnWaves * PPW];
-  __shared__ float red_l[kAttnWaves * PPW];
-  __shared__ float red_o[kAttnWaves * PPW][D];
+  constexpr int kSparseWaveEntries = E;
+  constexpr int LPP = D / 8;                        // lanes per position
+  constexpr int PPW = kWave / LPP;                  // positions per wave step
+  constexpr int NSTEP = kSparseWaveEntries / PPW;   // steps per round
+  __shared__ float red_m[kSparseMaxWaves * PPW];
+  __shared__ float red_l[kSparseMaxWaves * PPW];
+  __shared__ float red_o[kSparseMaxWaves * PPW][D];
 
   const int wid = blockIdx.x;
   const int xcd = wid & 7;
@@ -76,54 +89,67 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_partial_kernel(
   const int lo = s * chunk;
   const int hi = min(lo + chunk, k_max);
 
+  const int nwaves = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = lane / LPP;
   const int c = lane - p * LPP;
 
-  float qf[8];
-  unpack8(ld16(q + row * D + c * 8), qf);
+  // q slice of this lane as 4 packed bf16 pairs (dims c*8 .. c*8+7)
+  const uint4 qv = ld16(q + row * D + c * 8);
+  const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
 
   float m = -INFINITY, l = 0.f;
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
+  // Contiguous caches address rows of this (request, KV head) from one base with 32-bit
+  // offsets; paged caches translate every position through the page table.
+  const int64_t slab = PAGED ? 0 : (int64_t)(b * kv.num_kv_heads + h) * kv.max_len * D;
+  const uint16_t* kbase = kv.k + slab;
+  const uint16_t* vbase = kv.v + slab;
   const int32_t* irow = indices + row * k_max;
-  for (int e0 = lo + wave * PPW * U; e0 < hi; e0 += kAttnWaves * PPW * U) {
-    int idx[U];
-    bool ok[U];
+  for (int base = lo + wave * kSparseWaveEntries; base < hi; base += nwaves * kSparseWaveEntries) {
+    const int mine = base + lane < hi ? irow[base + lane] : -1;
+    // a round of padding (-1) or otherwise invalid entries issues no loads
+    if (__ballot(mine >= 0 && mine < vis) == 0ull) continue;
+    int idx[NSTEP];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e0 + u * PPW + p;
-      idx[u] = e < hi ? irow[e] : -1;
-      ok[u] = idx[u] >= 0 && idx[u] < vis;
+    for (int u = 0; u < NSTEP; ++u) idx[u] = __shfl(mine, u * PPW + p);
+    // Branch-free addresses: an entry outside [0, vis) reads position 0 (always present) and is
+    // masked out of the softmax below.
+    uint32_t okm = 0;
+    int64_t off[NSTEP];
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) {
+      const bool ok = idx[u] >= 0 && idx[u] < vis;
+      okm |= (uint32_t)ok << u;
+      const int n = ok ? idx[u] : 0;
+      if constexpr (PAGED)
+        off[u] = kv_row<D, true>(kv, b, h, n) + c * 8;
+      else
+        off[u] = (int64_t)n * D + c * 8;
     }
-    uint4 kr[U], vr[U];
+    uint4 kr[NSTEP], vr[NSTEP];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (ok[u]) {
-        const int64_t off = kv_row<D, PAGED>(kv, b, h, idx[u]) + c * 8;
-        kr[u] = ld16(kv.k + off);
-        vr[u] = ld16(kv.v + off);
-      }
+    for (int u = 0; u < NSTEP; ++u) {
+      kr[u] = ld16(kbase + off[u]);
+      vr[u] = ld16(vbase + off[u]);
     }
-    float sv[U];
+    float sv[NSTEP];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[8];
-      unpack8(kr[u], kf);
+    for (int u = 0; u < NSTEP; ++u) {
       float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], kf[i], dot);
+      dot = dot2_bf16(qw[0], kr[u].x, dot);
+      dot = dot2_bf16(qw[1], kr[u].y, dot);
+      dot = dot2_bf16(qw[2], kr[u].z, dot);
+      dot = dot2_bf16(qw[3], kr[u].w, dot);
       dot = group_sum<LPP>(dot);
-      sv[u] = ok[u] ? dot * scale_log2 : -INFINITY;
+      sv[u] = ((okm >> u) & 1u) ? dot * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[u]);
     }
-    float mx = sv[0];
-#pragma unroll
-    for (int u = 1; u < U; ++u) mx = fmaxf(mx, sv[u]);
     const float m_new = fmaxf(m, mx);
     if (m_new == -INFINITY) continue;
     const float alpha = fast_exp2(m - m_new);
@@ -131,7 +157,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_partial_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NSTEP; ++u) {
       const float pw = fast_exp2(sv[u] - m_new);
       l += pw;
       float vf[8];
@@ -150,13 +176,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_partial_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) red_o[slot][c * 8 + i] = o[i];
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int col = threadIdx.x;
+  const int nslots = nwaves * PPW;
+  for (int col = threadIdx.x; col < D; col += blockDim.x) {
     float M = -INFINITY;
-    for (int k = 0; k < kAttnWaves * PPW; ++k) M = fmaxf(M, red_m[k]);
+    for (int k = 0; k < nslots; ++k) M = fmaxf(M, red_m[k]);
     float Lsum = 0.f, O = 0.f;
     if (M != -INFINITY) {
-      for (int k = 0; k < kAttnWaves * PPW; ++k) {
+      for (int k = 0; k < nslots; ++k) {
         const float w = fast_exp2(red_m[k] - M);
         Lsum = fmaf(w, red_l[k], Lsum);
         O = fmaf(w, red_o[k][col], O);
@@ -168,21 +194,34 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_partial_kernel(
 
 // ============================================================================ combine
 // out = sum_s e^{m_s - M} o~_s / sum_s e^{m_s - M} l_s,  lse = (M + log2 sum_s e^{m_s - M} l_s) ln 2
-// with M = max_s m_s (m in log2 units).  One workgroup of D threads per row.
+// with M = max_s m_s (m in log2 units).  One workgroup of D threads per row; the split weights
+// e^{m_s - M} are computed once into LDS (dynamic, 2 * S floats).
 __global__ void combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                int S, int D, float* __restrict__ out, float* __restrict__ lse) {
+  extern __shared__ float cw[];  // [S] weights, then [S] weighted l
+  __shared__ float red[8];
   const int64_t row = blockIdx.x;
   const int col = threadIdx.x;
   const float* ml = part_ml + row * S * 2;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = col; s < S; s += blockDim.x) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((col & 63) == 0) red[col >> 6] = M;
+  __syncthreads();
+  M = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, red[w]);
+  for (int s = col; s < S; s += blockDim.x) {
+    const float w = M == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
+    cw[s] = w;
+    cw[S + s] = w * ml[2 * s + 1];
+  }
+  __syncthreads();
   float Lsum = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float w = fast_exp2(ml[2 * s] - M);
-      Lsum = fmaf(w, ml[2 * s + 1], Lsum);
-      O = fmaf(w, part_o[(row * S + s) * D + col], O);
-    }
+  const float* po = part_o + row * S * D + col;
+  for (int s = 0; s < S; ++s) {
+    Lsum += cw[S + s];
+    O = fmaf(cw[s], po[(int64_t)s * D], O);
   }
   out[row * D + col] = Lsum > 0.f ? O / Lsum : 0.f;
   if (col == 0) lse[row] = Lsum > 0.f ? (M + fast_log2(Lsum)) * kLn2 : -INFINITY;
@@ -201,7 +240,7 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
     float* __restrict__ lse) {
   constexpr int KS = D / 32;
   constexpr int DC = D / 64;  // output columns per lane
-  constexpr int U = 2;        // tiles in flight per wave
+  extern __shared__ int lds_pages[];          // paged caches: page ids of this chunk
   __shared__ __attribute__((aligned(16))) float pbuf[kAttnWaves][16][16];  // [wave][position][row]
   __shared__ float abuf[kAttnWaves][16];      // per-row rescale of the tile
   __shared__ float red_m[kAttnWaves][16];
@@ -257,39 +296,33 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
 #pragma unroll
     for (int d = 0; d < DC; ++d) o[r][d] = 0.f;
 
-  for (int n0 = start + wave * 16; n0 < end; n0 += kAttnWaves * 16 * U) {
-    uint4 kb[U][KS];
-    uint32_t vb[U][16];
+  if constexpr (PAGED) stage_pages(kv, b, start, end, lds_pages);
+  __syncthreads();
+
+  // Tiles of this wave: start + 16 * wave + 64 * it.  The K tile (MFMA B operand) and this lane's
+  // V columns of tile it+1 are loaded before tile it is processed.
+  auto load_tile = [&](int tile, uint4 (&kb)[KS], uint32_t (&vb)[16]) {
+    const int64_t base = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile);
+    const int nk = min(mm, L - 1 - tile);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tile = n0 + u * kAttnWaves * 16;
-      if (tile < end) {
-        const int64_t base = kv_tile<D, PAGED>(kv, b, h, tile);
-        const int nk = min(mm, L - 1 - tile);
+    for (int j = 0; j < KS; ++j) kb[j] = ld16(kv.k + base + (int64_t)nk * D + g4 * 8 + j * 32);
 #pragma unroll
-        for (int j = 0; j < KS; ++j) kb[u][j] = ld16(kv.k + base + (int64_t)nk * D + g4 * 8 + j * 32);
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-          const int nv = min(n, L - 1 - tile);
-          const uint16_t* vp = kv.v + base + (int64_t)nv * D + c0;
-          if constexpr (DC == 2)
-            vb[u][n] = *reinterpret_cast<const uint32_t*>(vp);
-          else
-            vb[u][n] = (uint32_t)(*vp);
-        }
-      }
+    for (int n = 0; n < 16; ++n) {
+      const int nv = min(n, L - 1 - tile);
+      const uint16_t* vp = kv.v + base + (int64_t)nv * D + c0;
+      if constexpr (DC == 2)
+        vb[n] = *reinterpret_cast<const uint32_t*>(vp);
+      else
+        vb[n] = (uint32_t)(*vp);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tile = n0 + u * kAttnWaves * 16;
-      if (tile >= end) break;
+  };
+  auto process = [&](int tile, const uint4 (&kc)[KS], const uint32_t (&vc)[16]) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+  #pragma unroll
       for (int j = 0; j < KS; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kb[u][j]),
-                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kc[j]), acc, 0, 0, 0);
       const int n = tile + mm;
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float sc = n < vis[i] ? acc[i] * scale_log2 : -INFINITY;
         const float tmax = group_max<16>(sc);
@@ -308,25 +341,25 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
         if (mm == 0) abuf[wave][4 * g4 + i] = alpha;
       }
       wave_lds_sync();
-#pragma unroll
+  #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const float al = abuf[wave][r];
-#pragma unroll
+  #pragma unroll
         for (int d = 0; d < DC; ++d) o[r][d] *= al;
       }
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
+  #pragma unroll
+      for (int nn = 0; nn < 16; ++nn) {
         float vf[DC];
         if constexpr (DC == 2) {
-          vf[0] = bf16_lo(vb[u][n]);
-          vf[1] = bf16_hi(vb[u][n]);
+          vf[0] = bf16_lo(vc[nn]);
+          vf[1] = bf16_hi(vc[nn]);
         } else {
-          vf[0] = bf16_lo(vb[u][n]);
+          vf[0] = bf16_lo(vc[nn]);
         }
-#pragma unroll
+  #pragma unroll
         for (int r4 = 0; r4 < MR; r4 += 4) {
-          const float4 pv = *reinterpret_cast<const float4*>(&pbuf[wave][n][r4]);
-#pragma unroll
+          const float4 pv = *reinterpret_cast<const float4*>(&pbuf[wave][nn][r4]);
+  #pragma unroll
           for (int d = 0; d < DC; ++d) {
             o[r4 + 0][d] = fmaf(pv.x, vf[d], o[r4 + 0][d]);
             o[r4 + 1][d] = fmaf(pv.y, vf[d], o[r4 + 1][d]);
@@ -336,6 +369,23 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
         }
       }
       wave_lds_sync();
+  };
+  // ping-pong buffers: tile it+1 loads while tile it is processed, with no register copies
+  // Prefetches are unconditional (a tile past the chunk reloads the chunk's last tile, which is
+  // cached) so the loads stay straight-line and the compiler's load counters stay exact.
+  uint4 ka[KS], kb2[KS];
+  uint32_t va[16], vb2[16];
+  constexpr int kStride = kAttnWaves * 16;
+  if (start < end) {
+    const int last = (end - 1) & ~15;
+    int tile = start + wave * 16;
+    load_tile(min(tile, last), ka, va);
+    for (; tile < end; tile += 2 * kStride) {
+      load_tile(min(tile + kStride, last), kb2, vb2);
+      process(tile, ka, va);
+      if (tile + kStride >= end) break;
+      load_tile(min(tile + 2 * kStride, last), ka, va);
+      process(tile + kStride, kb2, vb2);
     }
   }
 
@@ -381,7 +431,10 @@ static hipError_t launch_sparse_t(const AttnLaunch& a, hipStream_t stream) {
   const int n_groups = a.B * a.kv.num_kv_heads;
   const int items = a.GT * a.S;
   const int64_t blocks = 8LL * ((n_groups + 7) / 8) * items;
-  hipLaunchKernelGGL((sparse_partial_kernel<D, PAGED>), dim3((unsigned)blocks), dim3(kAttnThreads),
+  const int maxw = a.wave_entries == 64 ? kSparseMaxWaves : 4;
+  const int waves = a.waves < 1 ? 1 : (a.waves > maxw ? maxw : a.waves);
+  auto kern = a.wave_entries == 64 ? sparse_partial_kernel<D, PAGED, 64> : sparse_partial_kernel<D, PAGED, 32>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * kWave),
                      0, stream, a.q, a.kv, a.indices, a.T, a.Hq, a.G, a.k_max, a.scale_log2, a.S,
                      a.chunk, n_groups, items, a.part_o, a.part_ml, a.out, a.lse);
   return hipGetLastError();
@@ -389,7 +442,8 @@ static hipError_t launch_sparse_t(const AttnLaunch& a, hipStream_t stream) {
 
 static hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
   if (a.S == 1) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.rows), dim3(a.D), 0, stream, a.part_o, a.part_ml, a.S,
+  hipLaunchKernelGGL(combine_kernel, dim3(a.rows), dim3(a.D), 2 * a.S * sizeof(float), stream,
+                     a.part_o, a.part_ml, a.S,
                      a.D, a.out, a.lse);
   return hipGetLastError();
 }
@@ -407,7 +461,8 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t stream) {
 template <int D, bool PAGED, int MR>
 static hipError_t launch_dense_t(const AttnLaunch& a, hipStream_t stream) {
   dim3 grid(a.S, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
-  hipLaunchKernelGGL((dense_partial_kernel<D, PAGED, MR>), grid, dim3(kAttnThreads), 0, stream, a.q,
+  const size_t lds = PAGED ? ((size_t)(a.chunk >> a.kv.page_shift) + 2) * sizeof(int) : 0;
+  hipLaunchKernelGGL((dense_partial_kernel<D, PAGED, MR>), grid, dim3(kAttnThreads), lds, stream, a.q,
                      a.kv, a.T, a.Hq, a.G, a.scale_log2, a.S, a.chunk, a.part_o, a.part_ml, a.out,
                      a.lse);
   return hipGetLastError();

@@ -52,6 +52,15 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c for two packed bf16 pairs (v_dot2_f32_bf16; the bf16 products
+// are exact in float32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -95,11 +104,51 @@ __device__ __forceinline__ int64_t kv_row(const KVArgs& kv, int b, int h, int n)
   }
 }
 
-// Same, for a 16-aligned tile start n0 (every position of the tile lies in one page because
-// page sizes are powers of two >= 16): returns the offset of row n0; rows n0 + j follow at + j*D.
+// Same, for a 16-aligned tile start n0 that is uniform across the wave (every position of the
+// tile lies in one page because page sizes are powers of two >= 16): the page id is read with a
+// scalar load; returns the offset of row n0, rows n0 + j follow at + j*D.
 template <int D, bool PAGED>
 __device__ __forceinline__ int64_t kv_tile(const KVArgs& kv, int b, int h, int n0) {
-  return kv_row<D, PAGED>(kv, b, h, n0);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  if constexpr (!PAGED) {
+    return ((int64_t)(b * kv.num_kv_heads + h) * kv.max_len + n0) * D;
+  } else {
+    int page = __builtin_amdgcn_readfirstlane(
+        kv.page_table[(int64_t)b * kv.max_pages + (n0 >> kv.page_shift)]);
+    page = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
+    const int slot = n0 & ((1 << kv.page_shift) - 1);
+    return ((((int64_t)page * kv.num_kv_heads + h) << kv.page_shift) + slot) * D;
+  }
+}
+
+// Page ids of logical positions [start, end) of request b, clamped to the pool, copied into LDS
+// by the whole workgroup (paged caches only; the caller synchronises before use).  Entry i holds
+// the page of position ((start >> page_shift) + i) << page_shift.
+__device__ __forceinline__ void stage_pages(const KVArgs& kv, int b, int start, int end,
+                                            int* lds_pages) {
+  const int p0 = start >> kv.page_shift;
+  const int p1 = (end - 1) >> kv.page_shift;
+  const int32_t* pt = kv.page_table + (int64_t)b * kv.max_pages;
+  for (int i = threadIdx.x; i <= p1 - p0; i += blockDim.x) {
+    int page = pt[p0 + i];
+    lds_pages[i] = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
+  }
+}
+
+// Offset of row n0 (a wave-uniform, 16-aligned tile start inside [start, end)) using the page ids
+// staged by stage_pages; contiguous caches ignore the staging.
+template <int D, bool PAGED>
+__device__ __forceinline__ int64_t kv_tile_staged(const KVArgs& kv, const int* lds_pages, int start,
+                                                  int b, int h, int n0) {
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  if constexpr (!PAGED) {
+    return ((int64_t)(b * kv.num_kv_heads + h) * kv.max_len + n0) * D;
+  } else {
+    const int page = __builtin_amdgcn_readfirstlane(
+        lds_pages[(n0 >> kv.page_shift) - (start >> kv.page_shift)]);
+    const int slot = n0 & ((1 << kv.page_shift) - 1);
+    return ((((int64_t)page * kv.num_kv_heads + h) << kv.page_shift) + slot) * D;
+  }
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {

@@ -31,6 +31,8 @@ struct AttnLaunch {
   const int32_t* indices;  // sparse only
   int k_max;               // sparse only
   int S, chunk;
+  int waves;       // sparse only: waves per workgroup
+  int wave_entries;  // sparse only: index entries per wave round (64 or 32)
   float* part_o;   // [rows, S, D]
   float* part_ml;  // [rows, S, 2]
   float* out;
@@ -38,6 +40,7 @@ struct AttnLaunch {
 };
 
 size_t select_lds_bytes(int max_len);
+int score_threads(int GT);  // workgroup size of the score kernel for G*T query rows
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 hipError_t launch_sparse(const AttnLaunch& a, hipStream_t stream);

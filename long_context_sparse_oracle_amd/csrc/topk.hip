@@ -11,32 +11,38 @@
 namespace cs {
 
 constexpr int kHistBins = 4096;      // 12 leading bits of the ordered key
-constexpr int kScoreThreads = 256;   // 4 waves
+constexpr int kScoreMaxThreads = 1024;  // up to 16 waves (4 per 4 query rows of the group)
 constexpr int kScoreUnroll = 2;      // 16-position tiles in flight per wave
 constexpr int kSelThreads = 1024;    // 16 waves
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kCandCap = 8192;       // threshold-bin candidates held in LDS
+constexpr int kSelUnroll = 16;       // score loads in flight per lane in the select pass
 
 // ============================================================================ clear
+// Fills n 32-bit words (n a multiple of 4, p 16-byte aligned) with 16-byte stores.
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = value;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const uint4 v = make_uint4(value, value, value, value);
+  uint4* p4 = reinterpret_cast<uint4*>(p);
+  for (; i < n / 4; i += stride) p4[i] = v;
 }
 
 // ============================================================================ score + histogram
-// Grid: (chunks, B * Hkv, ceil(G*T / 16)).  One workgroup streams `chunk` positions of one
-// (request, KV head) and scores them against up to 16 of the G*T query rows that read that head
+// Grid: (chunks, B * Hkv, ceil(G*T / 16)).  One workgroup (4 waves per 4 query rows, so the
+// LDS histogram never starves a CU of waves) streams `chunk` positions of one (request, KV head)
+// and scores them against up to 16 of the G*T query rows that read that head
 // (row r = t * G + g, query head h * G + g).  Per 16-position tile a wave issues D/32
 // v_mfma_f32_16x16x32_bf16: A = the 16 query rows (lane l: row l%16, 8 dims), B = K^T (lane l:
 // position l%16, the same 8 dims), so each K row is read once for all rows of the group.
 // Scores of visible positions go to scores[row][n]; their 12-bit key prefix is counted in an LDS
 // histogram (two 16-bit counters per word) that is added to the global one at the end.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(kScoreThreads) void score_hist_kernel(
+__global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
-    float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk) {
-  extern __shared__ uint32_t lds_hist[];  // [rows_here][kHistBins / 2]
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk, int hist_rows) {
+  extern __shared__ uint32_t lds_hist[];  // [hist_rows][kHistBins / 2], then the chunk's page ids
+  int* lds_pages = reinterpret_cast<int*>(lds_hist + hist_rows * (kHistBins / 2));
   constexpr int KS = D / 32;              // MFMA k-steps per tile
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
@@ -51,7 +57,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_hist_kernel(
   if (start >= L) return;
   const int end = min(start + chunk, L);
 
-  for (int i = threadIdx.x; i < rows_here * (kHistBins / 2); i += kScoreThreads) lds_hist[i] = 0u;
+  for (int i = threadIdx.x; i < rows_here * (kHistBins / 2); i += blockDim.x) lds_hist[i] = 0u;
+  if constexpr (PAGED) stage_pages(kv, b, start, end, lds_pages);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,27 +97,35 @@ __global__ __launch_bounds__(kScoreThreads) void score_hist_kernel(
   }
   __syncthreads();
 
+  // Iteration `it` covers positions start + kStep * it .. + kStep; wave w scores the kScoreUnroll
+  // adjacent tiles at start + kStep * it + 16 * (kScoreUnroll * w + u), so each of its score
+  // stores per row fills consecutive 64-byte pieces of one line.  The K tiles of iteration it+1
+  // load while iteration it is scored (ping-pong buffers, no register copies); loads are
+  // unconditional (a tile past the chunk reloads the chunk's last tile, which is cached) so they
+  // stay straight-line and the compiler's load counters stay exact.
   const uint16_t* kbase = kv.k;
-  for (int n0 = start + wave * 16; n0 < end; n0 += 4 * 16 * kScoreUnroll) {
-    uint4 kb[kScoreUnroll][KS];
+  const int kStep = (int)(blockDim.x >> 6) * 16 * kScoreUnroll;
+  const int last = (end - 1) & ~15;
+  uint4 cur[kScoreUnroll][KS], nxt[kScoreUnroll][KS];
+  auto load_tiles = [&](int n0, uint4 (&dst)[kScoreUnroll][KS]) {
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int tile = n0 + u * 64;
-      if (tile < end) {
-        const int n = min(tile + m, L - 1);
-        const int64_t off = kv_row<D, PAGED>(kv, b, h, n) + g4 * 8;
+      const int tile = min(n0 + u * 16, last);
+      const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
+                          (int64_t)min(m, L - 1 - tile) * D + g4 * 8;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) kb[u][j] = ld16(kbase + off + j * 32);
-      }
+      for (int j = 0; j < KS; ++j) dst[u][j] = ld16(kbase + off + j * 32);
     }
+  };
+  auto score_tiles = [&](int n0, const uint4 (&kt)[kScoreUnroll][KS]) {
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int tile = n0 + u * 64;
+      const int tile = n0 + u * 16;
       if (tile >= end) break;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kb[u][j]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kt[u][j]),
                                                       acc, 0, 0, 0);
       const int n = tile + m;
 #pragma unroll
@@ -123,10 +138,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_hist_kernel(
         }
       }
     }
+  };
+  int n0 = start + wave * 16 * kScoreUnroll;
+  load_tiles(n0, cur);
+  for (; n0 < end; n0 += 2 * kStep) {
+    load_tiles(n0 + kStep, nxt);
+    score_tiles(n0, cur);
+    if (n0 + kStep >= end) break;
+    load_tiles(n0 + 2 * kStep, cur);
+    score_tiles(n0 + kStep, nxt);
   }
   __syncthreads();
 
-  for (int w = threadIdx.x; w < rows_here * (kHistBins / 2); w += kScoreThreads) {
+  for (int w = threadIdx.x; w < rows_here * (kHistBins / 2); w += blockDim.x) {
     const uint32_t v = lds_hist[w];
     if (v == 0u) continue;
     const int rl = w / (kHistBins / 2);
@@ -275,17 +299,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const bool fast = cntT <= (uint32_t)kCandCap;
   __syncthreads();
 
-  // ---- 2. mark keys above T12, collect keys in T12
-  for (int base = wave * 64; base < vis; base += kSelThreads * 2) {
-    float sv[2];
-    int nn[2];
+  // ---- 2. mark keys above T12, collect keys in T12 (kSelUnroll loads in flight per lane)
+  for (int base = wave * 64; base < vis; base += kSelThreads * kSelUnroll) {
+    float sv[kSelUnroll];
+    int nn[kSelUnroll];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kSelUnroll; ++u) {
       nn[u] = base + u * kSelThreads + lane;
       sv[u] = nn[u] < vis ? srow[nn[u]] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kSelUnroll; ++u) {
       const int nb = base + u * kSelThreads;
       if (nb >= vis) break;
       const bool valid = nn[u] < vis;
@@ -409,6 +433,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // ============================================================================ launchers
+int score_threads(int GT) {
+  const int rows = GT < 16 ? GT : 16;
+  return 256 * ((rows + 3) / 4);
+}
+
 size_t select_lds_bytes(int max_len) {
   const int words = ((max_len + 63) / 64) * 2;
   return sizeof(uint32_t) * ((size_t)kHistBins + 2 * (size_t)words + 2 * (size_t)kCandCap);
@@ -416,8 +445,9 @@ size_t select_lds_bytes(int max_len) {
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (n % 4 != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return hipErrorInvalidValue;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
   return hipGetLastError();
 }
@@ -425,15 +455,16 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
 template <int D, bool PAGED>
 static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
   const int rows_tile = a.GT < 16 ? a.GT : 16;
-  const size_t lds = (size_t)rows_tile * (kHistBins / 2) * sizeof(uint32_t);
+  const size_t page_ids = PAGED ? (size_t)(a.chunk >> a.kv.page_shift) + 2 : 0;
+  const size_t lds = (size_t)rows_tile * (kHistBins / 2) * sizeof(uint32_t) + page_ids * sizeof(int);
   auto kern = score_hist_kernel<D, PAGED>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.chunks, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
-  hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
-                     a.scale, a.scores, a.hist, a.chunk);
+  hipLaunchKernelGGL(kern, grid, dim3(score_threads(a.GT)), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
+                     a.scale, a.scores, a.hist, a.chunk, rows_tile);
   return hipGetLastError();
 }
 
