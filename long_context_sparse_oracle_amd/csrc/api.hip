@@ -109,9 +109,12 @@ void topk_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, i
   *chunks = (int)ceil_div(kv->max_len, c);
 }
 
+int64_t score_stride(const cs_kv_desc* kv) { return ceil_div(kv->max_len, 64) * 64; }
+
 size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) {
   const size_t rows = (size_t)rows_of(s);
-  return align_up(rows * (size_t)kv->max_len * sizeof(float)) + align_up(rows * 4096 * sizeof(uint32_t));
+  return align_up(rows * (size_t)score_stride(kv) * sizeof(float)) +
+         align_up(rows * 4096 * sizeof(uint32_t));
 }
 
 // ---- attention sizing
@@ -241,8 +244,9 @@ cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_de
   a.k_max = k_max;
   topk_chunking(shape, kv, &a.chunk, &a.chunks);
   char* ws = static_cast<char*>(workspace);
+  a.score_stride = score_stride(kv);
   a.scores = reinterpret_cast<float*>(ws);
-  a.hist = reinterpret_cast<uint32_t*>(ws + align_up((size_t)a.rows * kv->max_len * sizeof(float)));
+  a.hist = reinterpret_cast<uint32_t*>(ws + align_up((size_t)a.rows * a.score_stride * sizeof(float)));
   a.indices = indices;
   hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;

@@ -73,6 +73,11 @@ __device__ __forceinline__ uint32_t ord_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of ord_key: the float whose key is k.
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // ---------------------------------------------------------------------------- KV addressing
 struct KVArgs {
   const uint16_t* k;
@@ -127,11 +132,21 @@ __device__ __forceinline__ int64_t kv_tile(const KVArgs& kv, int b, int h, int n
 __device__ __forceinline__ void stage_pages(const KVArgs& kv, int b, int start, int end,
                                             int* lds_pages) {
   const int p0 = start >> kv.page_shift;
-  const int p1 = (end - 1) >> kv.page_shift;
-  const int32_t* pt = kv.page_table + (int64_t)b * kv.max_pages;
-  for (int i = threadIdx.x; i <= p1 - p0; i += blockDim.x) {
-    int page = pt[p0 + i];
-    lds_pages[i] = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
+  const int n = ((end - 1) >> kv.page_shift) - p0 + 1;
+  const int32_t* pt = kv.page_table + (int64_t)b * kv.max_pages + p0;
+  // 8 independent loads per thread in flight before any store
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * blockDim.x) {
+    int pg[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      pg[u] = i < n ? pt[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      if (i < n) lds_pages[i] = pg[u] < 0 ? 0 : (pg[u] >= kv.num_pages ? kv.num_pages - 1 : pg[u]);
+    }
   }
 }
 

@@ -17,7 +17,8 @@ struct TopkLaunch {
   const int32_t* k_per_req;
   int k_max;
   int chunk, chunks;
-  float* scores;    // [rows, max_len]
+  float* scores;    // [rows, score_stride]
+  int64_t score_stride;  // max_len rounded up to 64 floats
   uint32_t* hist;   // [rows, 4096]
   int32_t* indices; // [rows, k_max]
 };

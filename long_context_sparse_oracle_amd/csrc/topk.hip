@@ -16,7 +16,7 @@ constexpr int kScoreUnroll = 2;      // 16-position tiles in flight per wave
 constexpr int kSelThreads = 1024;    // 16 waves
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kCandCap = 8192;       // threshold-bin candidates held in LDS
-constexpr int kSelUnroll = 16;       // score loads in flight per lane in the select pass
+constexpr int kSelVecUnroll = 8;     // 16-byte score loads in flight per lane in the select pass
 
 // ============================================================================ clear
 // Fills n 32-bit words (n a multiple of 4, p 16-byte aligned) with 16-byte stores.
@@ -40,7 +40,8 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t va
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
-    float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk, int hist_rows) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk, int hist_rows,
+    int64_t score_stride) {
   extern __shared__ uint32_t lds_hist[];  // [hist_rows][kHistBins / 2], then the chunk's page ids
   int* lds_pages = reinterpret_cast<int*>(lds_hist + hist_rows * (kHistBins / 2));
   constexpr int KS = D / 32;              // MFMA k-steps per tile
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
     if (rl < rows_here) {
       const int t = r / G, gi = r - (r / G) * G;
       vis[i] = L - T + t + 1;
-      srow[i] = scores + ((((int64_t)b * T + t) * Hq + (h * G + gi)) * (int64_t)kv.max_len);
+      srow[i] = scores + (((int64_t)b * T + t) * Hq + (h * G + gi)) * score_stride;
     } else {
       vis[i] = 0;
       srow[i] = scores;
@@ -236,8 +237,9 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
 // Per row (b, t, hq): select the kk = min(k_b, visible) largest scores.
 //  1. threshold bin T12 of the 12-bit key prefix from the fused histogram (rebuilt from the scores
 //     when it does not add up to the visible count);
-//  2. one pass over the scores: keys above T12 are marked in an LDS bitmap (one ballot per 64
-//     positions), keys in T12 are appended to an LDS candidate list;
+//  2. one pass over the scores (16-byte loads): keys above T12 are marked in an LDS bitmap (8
+//     lanes' 4-bit nibbles OR-reduced per 32-bit word), keys in T12 are appended to an LDS
+//     candidate list;
 //  3. two 10-bit radix rounds over the candidates give the exact k-th key K* and how many keys
 //     equal to K* are taken (lowest positions first); when T12 holds more than kCandCap keys the
 //     rounds read the scores instead;
@@ -245,7 +247,7 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_req, int T, int Hq,
-    int max_len, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
+    int max_len, int64_t score_stride, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
   extern __shared__ uint32_t smem[];
   uint32_t* hist_s = smem;                      // kHistBins
   uint32_t* gt_bits = hist_s + kHistBins;       // bitmap_words
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
   const int kk = min(kb, vis);
   int32_t* out = indices + (int64_t)row * k_max;
-  const float* srow = scores + (int64_t)row * max_len;
+  const float* srow = scores + (int64_t)row * score_stride;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
@@ -273,16 +275,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     return;
   }
 
-  const int words = ((vis + 63) >> 6) * 2;  // bitmap words touched (64-position granules)
+  const int words = ((vis + 255) >> 8) * 8;  // bitmap words touched (256-position granules)
   for (int i = tid; i < words; i += kSelThreads) {
     gt_bits[i] = 0u;
     eq_bits[i] = 0u;
   }
   if (tid == 0) sh.cand_count = 0u;
 
+  // Scores are read 16 bytes (4 positions) per lane: iteration B covers kSelIter positions, wave w
+  // the 256-position blocks B + 256 * (kSelWaves * u + w).  The first iteration's loads are issued
+  // before the threshold search so they are in flight meanwhile.
+  constexpr int kSelIter = kSelThreads * 4 * kSelVecUnroll;
+  // the row's histogram: one 16-byte load per thread, issued first
+  static_assert(kHistBins == 4 * kSelThreads, "one uint4 of histogram bins per thread");
+  const uint4 hv = reinterpret_cast<const uint4*>(hist + (int64_t)row * kHistBins)[tid];
+  float4 sv[kSelVecUnroll];
+  auto load_iter = [&](int B) {
+#pragma unroll
+    for (int u = 0; u < kSelVecUnroll; ++u) {
+      const int n4 = B + (u * kSelWaves + wave) * 256 + lane * 4;
+      sv[u] = n4 < vis ? *reinterpret_cast<const float4*>(srow + n4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_iter(0);
+
   // ---- 1. threshold bin of the 12-bit prefix
-  const uint32_t* hrow = hist + (int64_t)row * kHistBins;
-  for (int i = tid; i < kHistBins; i += kSelThreads) hist_s[i] = hrow[i];
+  reinterpret_cast<uint4*>(hist_s)[tid] = hv;
   __syncthreads();
   uint32_t total = find_threshold<kHistBins / kSelThreads>(hist_s, kHistBins, (uint32_t)kk, sh);
   if (total != (uint32_t)vis || !sh.found) {
@@ -299,43 +317,76 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const bool fast = cntT <= (uint32_t)kCandCap;
   __syncthreads();
 
-  // ---- 2. mark keys above T12, collect keys in T12 (kSelUnroll loads in flight per lane)
-  for (int base = wave * 64; base < vis; base += kSelThreads * kSelUnroll) {
-    float sv[kSelUnroll];
-    int nn[kSelUnroll];
+  // ---- 2. mark keys above T12 in the bitmap, collect keys in T12
+  // A lane's 4 flags form a nibble; 8 lanes' nibbles OR-reduced with DPP give one 32-bit word.
+  // Candidate slots: ballots of all blocks first, then one LDS atomic per wave and iteration.
+  // bin(s) > T12  <=>  s >= lo_next,  bin(s) == T12  <=>  lo <= s < lo_next, where lo and lo_next
+  // are the smallest scores of bins T12 and T12 + 1 (the key map is monotone and float compares
+  // treat -0 and +0 as equal, like the keys); no score lies above bin 4095.
+  const float lo = key_to_float(T12 << 20);
+  const bool has_next = T12 < (uint32_t)(kHistBins - 1);
+  const float lo_next = has_next ? key_to_float((T12 + 1u) << 20) : 0.f;
+  auto process_iter = [&](int B) {
+    uint32_t eqm[kSelVecUnroll];
 #pragma unroll
-    for (int u = 0; u < kSelUnroll; ++u) {
-      nn[u] = base + u * kSelThreads + lane;
-      sv[u] = nn[u] < vis ? srow[nn[u]] : 0.f;
-    }
+    for (int u = 0; u < kSelVecUnroll; ++u) {
+      eqm[u] = 0u;
+      const int nb = B + (u * kSelWaves + wave) * 256;
+      if (nb >= vis) continue;
+      const int n4 = nb + lane * 4;
+      const float vals[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+      const uint32_t valid = n4 + 3 < vis ? 0xfu : (n4 >= vis ? 0u : (1u << (vis - n4)) - 1u);
+      uint32_t gt = 0u;
 #pragma unroll
-    for (int u = 0; u < kSelUnroll; ++u) {
-      const int nb = base + u * kSelThreads;
-      if (nb >= vis) break;
-      const bool valid = nn[u] < vis;
-      const uint32_t key = ord_key(sv[u]);
-      const uint32_t bin = key >> 20;
-      const uint64_t gm = __ballot(valid && bin > T12);
-      if (lane == 0) {
-        gt_bits[nb >> 5] = (uint32_t)gm;
-        gt_bits[(nb >> 5) + 1] = (uint32_t)(gm >> 32);
+      for (int j = 0; j < 4; ++j) {
+        const bool above = has_next && vals[j] >= lo_next;
+        gt |= (uint32_t)above << j;
+        eqm[u] |= (uint32_t)(!above && vals[j] >= lo) << j;
       }
-      if (fast) {
-        const bool eq = valid && bin == T12;
-        const uint64_t em = __ballot(eq);
-        if (em) {
-          uint32_t slot0 = 0;
-          if (lane == 0) slot0 = atomicAdd(&sh.cand_count, (uint32_t)__popcll(em));
-          slot0 = __shfl(slot0, 0);
-          const uint32_t slot = slot0 + __builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
-          if (eq && slot < (uint32_t)kCandCap) {
-            cand_key[slot] = key;
-            cand_pos[slot] = (uint32_t)nn[u];
+      gt &= valid;
+      eqm[u] &= valid;
+      uint32_t word = gt << (4 * (lane & 7));
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xf, 0xf, false);
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xf, 0xf, false);
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x141, 0xf, 0xf, false);
+      if ((lane & 7) == 0) gt_bits[(nb >> 5) + (lane >> 3)] = word;
+    }
+    if (!fast) return;
+    // per-lane candidate count over all blocks, wave prefix via ballots of its 5 bits
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kSelVecUnroll; ++u) cnt += __popc(eqm[u]);
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t bm = __ballot((cnt >> bit) & 1u);
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
+      tot += (uint32_t)__popcll(bm) << bit;
+    }
+    if (tot == 0) return;
+    uint32_t slot0 = 0;
+    if (lane == 0) slot0 = atomicAdd(&sh.cand_count, tot);
+    uint32_t slot = __shfl(slot0, 0) + before;
+#pragma unroll
+    for (int u = 0; u < kSelVecUnroll; ++u) {
+      if (eqm[u] == 0u) continue;
+      const int n4 = B + (u * kSelWaves + wave) * 256 + lane * 4;
+      const float vals[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((eqm[u] >> j) & 1u) {
+          if (slot < (uint32_t)kCandCap) {
+            cand_key[slot] = ord_key(vals[j]);
+            cand_pos[slot] = (uint32_t)(n4 + j);
           }
+          ++slot;
         }
       }
     }
+  };
+  for (int B = 0; B < vis; B += kSelIter) {
+    if (B > 0) load_iter(B);
+    process_iter(B);
   }
   __syncthreads();
 
@@ -439,7 +490,7 @@ int score_threads(int GT) {
 }
 
 size_t select_lds_bytes(int max_len) {
-  const int words = ((max_len + 63) / 64) * 2;
+  const int words = ((max_len + 255) / 256) * 8;
   return sizeof(uint32_t) * ((size_t)kHistBins + 2 * (size_t)words + 2 * (size_t)kCandCap);
 }
 
@@ -464,7 +515,7 @@ static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
   }
   dim3 grid(a.chunks, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
   hipLaunchKernelGGL(kern, grid, dim3(score_threads(a.GT)), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
-                     a.scale, a.scores, a.hist, a.chunk, rows_tile);
+                     a.scale, a.scores, a.hist, a.chunk, rows_tile, a.score_stride);
   return hipGetLastError();
 }
 
@@ -481,10 +532,10 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
     e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int words = ((a.kv.max_len + 63) / 64) * 2;
+  const int words = ((a.kv.max_len + 255) / 256) * 8;
   hipLaunchKernelGGL(select_kernel, dim3(a.rows), dim3(kSelThreads), lds, stream, a.scores,
-                     a.hist, a.kv.seq_lens, a.k_per_req, a.T, a.Hq, a.kv.max_len, a.k_max, words,
-                     a.indices);
+                     a.hist, a.kv.seq_lens, a.k_per_req, a.T, a.Hq, a.kv.max_len, a.score_stride,
+                     a.k_max, words, a.indices);
   return hipGetLastError();
 }
 
