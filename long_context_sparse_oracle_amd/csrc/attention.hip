@@ -425,6 +425,192 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
   }
 }
 
+// ============================================================================ dense partial, MFMA P.V
+// For G*T >= 5 query rows per KV head the float32 P.V of dense_partial_kernel is VALU-bound, so
+// here both products run on MFMA.  Scores are computed as K q^T (A = 16 tokens x 32 dims of K,
+// B = the query rows): lane l then holds tokens 4*(l/16)..+3 of query row l%16, which is exactly
+// the A-operand layout of v_mfma_f32_16x16x16_bf16 for P (rows x tokens).  P is split into bf16
+// hi + lo parts (two MFMAs, ~16 significant bits), V (tokens x dims, bf16) is staged row-major in
+// a per-wave LDS buffer and read as the B operand with ds_read_b64_tr_b16 (lane s of 16-lane
+// group g addresses token 4g + s/4, dims 16 nb + 4 (s%4); the transpose hands lane i the
+// values of tokens 4g..4g+3 at dim 16 nb + i).  The running max of a row is raised only when a
+// tile exceeds it by more than 2^8 (in log2 units), so O is rescaled rarely; P <= 2^8 is exact
+// enough in hi + lo bf16.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kAttnThreads) void dense_partial_mfma_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale_log2, int S,
+    int chunk, float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int KS = D / 32;        // k-steps of K q^T
+  constexpr int NB = D / 16;        // 16-column blocks of P.V
+  constexpr int VROW = D * 2 + 32;  // LDS bytes per staged V token (padded against bank conflicts)
+  constexpr int VLD = D / 32;       // 16-byte V loads per lane per tile
+  constexpr int VBUF = 16 * VROW;   // bytes per wave
+  constexpr int RED = kAttnWaves * 16 * D * 4;  // final merge of the waves' O tiles
+  constexpr int SHARED = (kAttnWaves * VBUF > RED) ? kAttnWaves * VBUF : RED;
+  extern __shared__ int lds_pages[];
+  __shared__ __attribute__((aligned(16))) char smem[SHARED];
+  __shared__ float red_m[kAttnWaves][16];
+  __shared__ float red_l[kAttnWaves][16];
+
+  const int s = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int mt = blockIdx.z;
+  const int Hkv = kv.num_kv_heads;
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int GT = G * T;
+  const int r0 = mt * 16;
+  const int rows_here = min(16, GT - r0);
+  const int L = seq_len_of(kv, b);
+  const int start = s * chunk;
+  const int end = min(start + chunk, L);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mm = lane & 15;   // query row (softmax layout) / token of the K operand
+  const int g4 = lane >> 4;
+
+  bf16x8 qb[KS];
+  int vis_row = 0;
+  {
+    const int r = r0 + mm;
+    if (mm < rows_here) {
+      const int t = r / G, gi = r - (r / G) * G;
+      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qb[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+      vis_row = L - T + t + 1;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qb[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  }
+  float m_row = -INFINITY;  // running max of row mm (log2 units)
+  float l_part = 0.f;       // this lane's share of the row sum
+  f32x4 oacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (PAGED) stage_pages(kv, b, start, end, lds_pages);
+  __syncthreads();
+
+  char* vb = smem + wave * VBUF;
+  auto load_tile = [&](int tile, uint4 (&kt)[KS], uint4 (&vt)[VLD]) {
+    const int64_t base = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile);
+    const int nk = min(mm, L - 1 - tile);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kt[j] = ld16(kv.k + base + (int64_t)nk * D + g4 * 8 + j * 32);
+    const int nv = min(lane >> 2, L - 1 - tile);
+#pragma unroll
+    for (int x = 0; x < VLD; ++x) vt[x] = ld16(kv.v + base + (int64_t)nv * D + (lane & 3) * (D / 4) + x * 8);
+  };
+  auto process = [&](int tile, const uint4 (&kt)[KS], const uint4 (&vt)[VLD]) {
+#pragma unroll
+    for (int x = 0; x < VLD; ++x)
+      *reinterpret_cast<uint4*>(vb + (lane >> 2) * VROW + (lane & 3) * (D / 2) + x * 16) = vt[x];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[j]), qb[j], acc, 0, 0, 0);
+    float sc[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = tile + 4 * g4 + i < vis_row ? acc[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool raise = tmax > m_row + 8.f;
+    if (__ballot(raise)) {
+      const float m_new = raise ? tmax : m_row;
+      const float alpha = m_row == -INFINITY ? 0.f : fast_exp2(m_row - m_new);
+      l_part *= alpha;
+      m_row = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][i] *= ai;
+      }
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = sc[i] == -INFINITY ? 0.f : fast_exp2(sc[i] - m_row);
+      l_part += p;
+      const uint32_t pb = __float_as_uint(p);
+      hi[i] = pb >> 16;
+      lo[i] = __float_as_uint(p - __uint_as_float(pb & 0xffff0000u)) >> 16;
+    }
+    const v4i16 ahi = __builtin_bit_cast(v4i16, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+    const v4i16 alo = __builtin_bit_cast(v4i16, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    wave_lds_sync();
+    const char* vrd = vb + (4 * g4 + (mm >> 2)) * VROW + 4 * (mm & 3) * 2;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4i16 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(vrd + nb * 32));
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, oacc[nb], 0, 0, 0);
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, oacc[nb], 0, 0, 0);
+    }
+    wave_lds_sync();
+  };
+
+  uint4 ka[KS], kb2[KS], va[VLD], vb2[VLD];
+  constexpr int kStride = kAttnWaves * 16;
+  if (start < end) {
+    const int last = (end - 1) & ~15;
+    int tile = start + wave * 16;
+    load_tile(min(tile, last), ka, va);
+    for (; tile < end; tile += 2 * kStride) {
+      load_tile(min(tile + kStride, last), kb2, vb2);
+      process(tile, ka, va);
+      if (tile + kStride >= end) break;
+      load_tile(min(tile + 2 * kStride, last), ka, va);
+      process(tile + kStride, kb2, vb2);
+    }
+  }
+
+  // row sums over the 4 lanes holding a row; merge the waves
+  float l_row = l_part + __shfl_xor(l_part, 16);
+  l_row += __shfl_xor(l_row, 32);
+  __syncthreads();  // every wave is done with its V buffer before the merge area reuses it
+  float* red_o = reinterpret_cast<float*>(smem);  // [wave][16 rows][D]
+  if (g4 == 0) {
+    red_m[wave][mm] = m_row;
+    red_l[wave][mm] = l_row;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_o[(wave * 16 + 4 * g4 + i) * D + nb * 16 + mm] = oacc[nb][i];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < rows_here * D; idx += kAttnThreads) {
+    const int rl = idx / D;
+    const int col = idx - rl * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, red_m[w][rl]);
+    float Lsum = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float wt = fast_exp2(red_m[w][rl] - M);
+        Lsum = fmaf(wt, red_l[w][rl], Lsum);
+        O = fmaf(wt, red_o[(w * 16 + rl) * D + col], O);
+      }
+    }
+    const int r = r0 + rl;
+    const int t = r / G, gi = r - (r / G) * G;
+    const int64_t row = ((int64_t)b * T + t) * Hq + (h * G + gi);
+    store_result(O, M, Lsum, col, D, row, s, S, part_o, part_ml, out, lse);
+  }
+}
+
 // ============================================================================ launchers
 template <int D, bool PAGED>
 static hipError_t launch_sparse_t(const AttnLaunch& a, hipStream_t stream) {
@@ -469,11 +655,21 @@ static hipError_t launch_dense_t(const AttnLaunch& a, hipStream_t stream) {
 }
 
 template <int D, bool PAGED>
+static hipError_t launch_dense_mfma_t(const AttnLaunch& a, hipStream_t stream) {
+  dim3 grid(a.S, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
+  const size_t lds = PAGED ? ((size_t)(a.chunk >> a.kv.page_shift) + 2) * sizeof(int) : 0;
+  hipLaunchKernelGGL((dense_partial_mfma_kernel<D, PAGED>), grid, dim3(kAttnThreads), lds, stream,
+                     a.q, a.kv, a.T, a.Hq, a.G, a.scale_log2, a.S, a.chunk, a.part_o, a.part_ml,
+                     a.out, a.lse);
+  return hipGetLastError();
+}
+
+// Up to 4 query rows per KV head: float32 P.V on the VALU is cheap enough; more rows: MFMA P.V.
+template <int D, bool PAGED>
 static hipError_t launch_dense_d(const AttnLaunch& a, hipStream_t stream) {
   const int rows_tile = a.GT < 16 ? a.GT : 16;
   if (rows_tile <= 4) return launch_dense_t<D, PAGED, 4>(a, stream);
-  if (rows_tile <= 8) return launch_dense_t<D, PAGED, 8>(a, stream);
-  return launch_dense_t<D, PAGED, 16>(a, stream);
+  return launch_dense_mfma_t<D, PAGED>(a, stream);
 }
 
 hipError_t launch_dense(const AttnLaunch& a, hipStream_t stream) {
