@@ -123,23 +123,21 @@ size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) {
 // waves (no partials to merge).  Larger calls use E = 32 and 4-wave workgroups, several per CU,
 // so load and compute phases of different workgroups overlap.
 struct SparsePlan {
-  int S, chunk, waves, wave_entries;
+  int S, chunk, waves;
 };
 
 SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
+  // One workgroup of up to kSparseWaves waves per row, looping over its list kSparseWaveEntries
+  // entries per wave and round: no partials and no combine pass.  Only when there are fewer rows
+  // than compute units are lists split, to put every unit to work.
   const int64_t rows = rows_of(s);
-  const bool one_generation = rows * ceil_div(k_max, 64) <= 12LL * cu_count();
-  const int E = one_generation ? 64 : 32;
-  const int maxw = one_generation ? 12 : 4;
-  const int64_t waves_needed = ceil_div(k_max, E);
+  const int64_t waves_needed = ceil_div(k_max, cs::kSparseWaveEntries);
   int64_t S;
   if (requested > 0) {
     S = requested;
   } else {
-    S = ceil_div(waves_needed, maxw);
-    const int64_t spread = ceil_div(cu_count(), rows);
-    const int64_t cap = waves_needed < spread ? waves_needed : spread;
-    if (S < cap) S = cap;
+    S = rows >= cu_count() ? 1 : ceil_div(cu_count(), rows);
+    if (S > waves_needed) S = waves_needed;
   }
   if (S > k_max) S = k_max;
   if (S > 1024) S = 1024;
@@ -148,9 +146,8 @@ SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
   SparsePlan p;
   p.S = (int)ceil_div(k_max, chunk);
   p.chunk = (int)chunk;
-  const int64_t w = ceil_div(chunk, E);
-  p.waves = (int)(w > maxw ? maxw : w);
-  p.wave_entries = E;
+  const int64_t w = ceil_div(chunk, cs::kSparseWaveEntries);
+  p.waves = (int)(w > cs::kSparseWaves ? cs::kSparseWaves : w);
   return p;
 }
 
@@ -291,7 +288,6 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   a.S = S;
   a.chunk = plan.chunk;
   a.waves = plan.waves;
-  a.wave_entries = plan.wave_entries;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
@@ -340,7 +336,6 @@ cs_status dense_decode_attn(const cs_decode_shape* shape, const void* q, const c
   a.S = S;
   a.chunk = chunk;
   a.waves = 0;
-  a.wave_entries = 0;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))

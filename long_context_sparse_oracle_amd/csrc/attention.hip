@@ -38,36 +38,30 @@ __device__ __forceinline__ void store_result(float O, float M, float Lsum, int c
 }
 
 // ============================================================================ sparse partial
-// One workgroup per (row, split): W waves (blockDim.x = 64 W), each gathering kSparseWaveEntries
-// entries of the row's index list per round.  Rows of one (request, KV head) are kept on one XCD
-// (workgroup w runs on XCD w % 8, so group g gets the ids congruent to g mod 8): rows of a GQA
-// group that pick the same token find its K/V lines in that XCD's L2.
-// Per round a wave loads its indices with one coalesced load, hands them to the lanes with
-// ds_bpermute, then issues every K and V load of the round before using any of them: D/8 lanes
-// hold one position (8 dims = 16 bytes of K and of V), 64/(D/8) positions per step, so a round
-// keeps 64 whole rows (32 KB of K and V at D=128) in flight per wave.  Scores are reduced across the D/8
-// lanes with DPP, the round's softmax statistics are merged into the running (m, l, o) and, at
-// the end, the waves' and position groups' states are merged through LDS.
-constexpr int kSparseMaxWaves = 12;
-
-// E = entries per wave round: 64 for calls whose waves all fit on the GPU at once (whole lists
-// in one workgroup of up to 12 waves), 32 for larger calls (4-wave workgroups at >= 5 waves per
-// SIMD, so many rounds of different workgroups overlap).
-template <int D, bool PAGED, int E>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64, E == 64 ? kSparseMaxWaves * 64 : 256),
-                               amdgpu_waves_per_eu(E == 64 ? 3 : 5)))
+// One workgroup per (row, split) of up to MAXW waves; each wave takes E entries of the row's
+// index list per round and loops, so many short rounds of different waves overlap and the data
+// that arrives last leaves little compute behind it.  Rows of one (request, KV head) are kept on
+// one XCD (workgroup w runs on XCD w % 8, so group g gets the ids congruent to g mod 8): rows of
+// a GQA group that pick the same token find its K/V lines in that XCD's L2.
+// Indices are loaded one round ahead with one coalesced load and handed to the lanes with
+// ds_bpermute; a round then issues all of its K loads and then all of its V loads before using
+// any: D/8 lanes hold one position (8 dims = 16 bytes of K and of V), 64/(D/8) positions per
+// step.  Scores are reduced across the D/8 lanes with DPP, the round's softmax statistics are
+// merged into the running (m, l, o); at the end the wave's position groups are merged with lane
+// shuffles and the waves through LDS.
+template <int D, bool PAGED, int E, int MAXW>
+__global__ void __launch_bounds__(MAXW * 64)
 sparse_partial_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, const int32_t* __restrict__ indices, int T, int Hq,
     int G, int k_max, float scale_log2, int S, int chunk, int n_groups, int items_per_group,
     float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ out,
     float* __restrict__ lse) {
-  constexpr int kSparseWaveEntries = E;
   constexpr int LPP = D / 8;                        // lanes per position
   constexpr int PPW = kWave / LPP;                  // positions per wave step
-  constexpr int NSTEP = kSparseWaveEntries / PPW;   // steps per round
-  __shared__ float red_m[kSparseMaxWaves * PPW];
-  __shared__ float red_l[kSparseMaxWaves * PPW];
-  __shared__ float red_o[kSparseMaxWaves * PPW][D];
+  constexpr int NSTEP = E / PPW;                    // steps per round
+  __shared__ float red_m[MAXW];
+  __shared__ float red_l[MAXW];
+  __shared__ float red_o[MAXW][D];
 
   const int wid = blockIdx.x;
   const int xcd = wid & 7;
@@ -84,8 +78,7 @@ sparse_partial_kernel(
   const int hq = h * G + gi;
   const int64_t row = ((int64_t)b * T + t) * Hq + hq;
 
-  const int L = seq_len_of(kv, b);
-  const int vis = L - T + t + 1;
+  const int vis = seq_len_vec(kv, b) - T + t + 1;  // per lane, wanted only by the validity test
   const int lo = s * chunk;
   const int hi = min(lo + chunk, k_max);
 
@@ -110,8 +103,16 @@ sparse_partial_kernel(
   const uint16_t* kbase = kv.k + slab;
   const uint16_t* vbase = kv.v + slab;
   const int32_t* irow = indices + row * k_max;
-  for (int base = lo + wave * kSparseWaveEntries; base < hi; base += nwaves * kSparseWaveEntries) {
-    const int mine = base + lane < hi ? irow[base + lane] : -1;
+  // Index loads run one round ahead of the gathers, and the first is issued next to the q load,
+  // so neither waits for the other.  They are unconditional and clamped to the last entry of the
+  // split (k_max >= 1 makes hi - 1 a valid entry): the compiler then counts them like the
+  // gathers and never has to drain the memory counter at the loop head.
+  const int round_step = nwaves * E;
+  int base = lo + wave * E;
+  int next_idx = irow[min(base + lane, hi - 1)];
+  for (; base < hi; base += round_step) {
+    const int mine = base + lane < hi ? next_idx : -1;
+    next_idx = irow[min(base + round_step + lane, hi - 1)];
     // a round of padding (-1) or otherwise invalid entries issues no loads
     if (__ballot(mine >= 0 && mine < vis) == 0ull) continue;
     int idx[NSTEP];
@@ -131,12 +132,15 @@ sparse_partial_kernel(
       else
         off[u] = (int64_t)n * D + c * 8;
     }
+    // every K load before any V load: the scores and their max can be formed while V arrives
     uint4 kr[NSTEP], vr[NSTEP];
 #pragma unroll
-    for (int u = 0; u < NSTEP; ++u) {
-      kr[u] = ld16(kbase + off[u]);
-      vr[u] = ld16(vbase + off[u]);
-    }
+    for (int u = 0; u < NSTEP; ++u) kr[u] = ld16(kbase + off[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) vr[u] = ld16(vbase + off[u]);
+    // keep the scheduler from pulling score math (and its waits) in between the loads
+    __builtin_amdgcn_sched_barrier(0);
     float sv[NSTEP];
     float mx = -INFINITY;
 #pragma unroll
@@ -168,15 +172,31 @@ sparse_partial_kernel(
     m = m_new;
   }
 
-  const int slot = wave * PPW + p;
-  if (c == 0) {
+  // merge the wave's PPW position groups (lanes c + LPP p) with lane shuffles, then the waves
+  // through LDS
+#pragma unroll
+  for (int x = LPP; x < kWave; x *= 2) {
+    const float m_o = __shfl_xor(m, x);
+    const float l_o = __shfl_xor(l, x);
+    const float M = fmaxf(m, m_o);
+    const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float bw = m_o == -INFINITY ? 0.f : fast_exp2(m_o - M);
+    l = a * l + bw * l_o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = a * o[i] + bw * __shfl_xor(o[i], x);
+    m = M;
+  }
+  const int slot = wave;
+  if (lane == 0) {
     red_m[slot] = m;
     red_l[slot] = l;
   }
+  if (p == 0) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red_o[slot][c * 8 + i] = o[i];
+    for (int i = 0; i < 8; ++i) red_o[slot][c * 8 + i] = o[i];
+  }
   __syncthreads();
-  const int nslots = nwaves * PPW;
+  const int nslots = nwaves;
   for (int col = threadIdx.x; col < D; col += blockDim.x) {
     float M = -INFINITY;
     for (int k = 0; k < nslots; ++k) M = fmaxf(M, red_m[k]);
@@ -617,12 +637,11 @@ static hipError_t launch_sparse_t(const AttnLaunch& a, hipStream_t stream) {
   const int n_groups = a.B * a.kv.num_kv_heads;
   const int items = a.GT * a.S;
   const int64_t blocks = 8LL * ((n_groups + 7) / 8) * items;
-  const int maxw = a.wave_entries == 64 ? kSparseMaxWaves : 4;
-  const int waves = a.waves < 1 ? 1 : (a.waves > maxw ? maxw : a.waves);
-  auto kern = a.wave_entries == 64 ? sparse_partial_kernel<D, PAGED, 64> : sparse_partial_kernel<D, PAGED, 32>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * kWave),
-                     0, stream, a.q, a.kv, a.indices, a.T, a.Hq, a.G, a.k_max, a.scale_log2, a.S,
-                     a.chunk, n_groups, items, a.part_o, a.part_ml, a.out, a.lse);
+  const int waves = a.waves < 1 ? 1 : (a.waves > kSparseWaves ? kSparseWaves : a.waves);
+  hipLaunchKernelGGL((sparse_partial_kernel<D, PAGED, kSparseWaveEntries, kSparseWaves>),
+                     dim3((unsigned)blocks), dim3(waves * kWave), 0, stream, a.q, a.kv, a.indices,
+                     a.T, a.Hq, a.G, a.k_max, a.scale_log2, a.S, a.chunk, n_groups, items,
+                     a.part_o, a.part_ml, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -96,6 +96,16 @@ __device__ __forceinline__ int seq_len_of(const KVArgs& kv, int b) {
   return L < 0 ? 0 : (L > kv.max_len ? kv.max_len : L);
 }
 
+// The same value held in a vector register, for kernels that need it only after their first
+// vector loads: a scalar load shares the scalar counter with the kernel-argument loads, whose
+// out-of-order returns make every wait on that counter wait for all of them, so the first
+// vector loads would queue behind this cold read; as a vector load nothing waits for it until
+// its first use.
+__device__ __forceinline__ int seq_len_vec(const KVArgs& kv, int b) {
+  const int L = __hip_atomic_load(kv.seq_lens + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return L < 0 ? 0 : (L > kv.max_len ? kv.max_len : L);
+}
+
 // Element offset of row (b, h, n) in the K or V buffer; n must be < L_b.
 template <int D, bool PAGED>
 __device__ __forceinline__ int64_t kv_row(const KVArgs& kv, int b, int h, int n) {

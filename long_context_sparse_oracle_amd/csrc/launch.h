@@ -8,6 +8,10 @@
 
 namespace cs {
 
+// Sparse attention launch shape: index entries a wave takes per round, and waves per workgroup.
+constexpr int kSparseWaveEntries = 16;
+constexpr int kSparseWaves = 8;
+
 struct TopkLaunch {
   const uint16_t* q;
   KVArgs kv;
@@ -33,7 +37,6 @@ struct AttnLaunch {
   int k_max;               // sparse only
   int S, chunk;
   int waves;       // sparse only: waves per workgroup
-  int wave_entries;  // sparse only: index entries per wave round (64 or 32)
   float* part_o;   // [rows, S, D]
   float* part_ml;  // [rows, S, 2]
   float* out;
