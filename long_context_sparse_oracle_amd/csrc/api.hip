@@ -109,13 +109,56 @@ void topk_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, i
   *chunks = (int)ceil_div(kv->max_len, c);
 }
 
-int64_t score_stride(const cs_kv_desc* kv) { return ceil_div(kv->max_len, 64) * 64; }
+// Filtered indexer (candidates only) for lists of at most 1/16 of the cache; its score pass
+// runs 4-wave workgroups over chunks of >= 1024 positions, about 16 per compute unit over the
+// call, so ragged lengths still leave the last wave of workgroups short.
 
-size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) {
-  const size_t rows = (size_t)rows_of(s);
-  return align_up(rows * (size_t)score_stride(kv) * sizeof(float)) +
-         align_up(rows * 4096 * sizeof(uint32_t));
+void cand_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, int* chunks) {
+  const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
+  const int64_t target = 16LL * cu_count();
+  int64_t c = ceil_div(groups * kv->max_len, target);
+  c = ceil_div(c, 256) * 256;
+  if (c < 1024) c = 1024;
+  if (c > 16384) c = 16384;
+  *chunk = (int)c;
+  *chunks = (int)ceil_div(kv->max_len, c);
 }
+
+// Per-row pitch (floats) of the score area: the scores of every position, or the candidate slots
+// of the filtered indexer (half a pair per position of every chunk).
+int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  int cc, cn;
+  cand_chunking(s, kv, &cc, &cn);
+  const int64_t dense = ceil_div(kv->max_len, 64) * 64;
+  const int64_t cand = (int64_t)cc * cn;
+  return dense > cand ? dense : cand;
+}
+
+// The candidate pass addresses the rows of one (request, KV head) through a buffer resource,
+// whose size field is 32-bit: their score areas must span less than 2 GiB.
+bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
+  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
+  return (int64_t)k_max * 16 <= kv->max_len && span < (1LL << 31);
+}
+
+struct TopkWs {
+  size_t scores, hist, keys, counts, total;
+};
+
+TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  const size_t rows = (size_t)rows_of(s);
+  int cc, cn;
+  cand_chunking(s, kv, &cc, &cn);
+  TopkWs w;
+  w.scores = 0;
+  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.keys = w.hist + align_up(rows * 4096 * sizeof(uint32_t));
+  w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
+  w.total = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  return w;
+}
+
+size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) { return topk_ws_layout(s, kv).total; }
 
 // ---- attention sizing
 // Gather plan.  A wave handles one round of E index entries.  When every wave of the call fits
@@ -240,10 +283,15 @@ cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_de
   a.k_per_req = k_per_req;
   a.k_max = k_max;
   topk_chunking(shape, kv, &a.chunk, &a.chunks);
+  cand_chunking(shape, kv, &a.cand_chunk, &a.cand_chunks);
+  a.filtered = topk_filtered(shape, kv, k_max);
   char* ws = static_cast<char*>(workspace);
-  a.score_stride = score_stride(kv);
-  a.scores = reinterpret_cast<float*>(ws);
-  a.hist = reinterpret_cast<uint32_t*>(ws + align_up((size_t)a.rows * a.score_stride * sizeof(float)));
+  const TopkWs lay = topk_ws_layout(shape, kv);
+  a.score_stride = score_stride(shape, kv);
+  a.scores = reinterpret_cast<float*>(ws + lay.scores);
+  a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
+  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
+  a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.indices = indices;
   hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;

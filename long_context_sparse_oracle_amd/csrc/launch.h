@@ -25,6 +25,11 @@ struct TopkLaunch {
   int64_t score_stride;  // max_len rounded up to 64 floats
   uint32_t* hist;   // [rows, 4096]
   int32_t* indices; // [rows, k_max]
+  // filtered indexer (k_max <= max_len / 16): sampled thresholds, then candidates only
+  bool filtered;
+  uint32_t* sample_keys;  // [rows, 1024]: ordered keys of the sampled scores
+  uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
+  int cand_chunk, cand_chunks;
 };
 
 struct AttnLaunch {

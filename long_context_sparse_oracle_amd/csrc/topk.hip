@@ -10,6 +10,8 @@
 
 namespace cs {
 
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+
 constexpr int kHistBins = 4096;      // 12 leading bits of the ordered key
 constexpr int kScoreMaxThreads = 1024;  // up to 16 waves (4 per 4 query rows of the group)
 constexpr int kScoreUnroll = 2;      // 16-position tiles in flight per wave
@@ -165,31 +167,23 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
 }
 
 // ============================================================================ select
-// Block-wide exclusive prefix sum over kSelThreads values.
+// Block-wide exclusive prefix sum over the NW * 64 threads' values.
+template <int NW = kSelWaves>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t t = wsum[w];
-      wsum[w] = acc;
-      acc += t;
-    }
-    wsum[kSelWaves] = acc;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = wsum[w];
+    before += w < wave ? t : 0u;
+    all += t;
   }
-  __syncthreads();
-  const uint32_t r = wsum[wave] + x - v;
-  if (total) *total = wsum[kSelWaves];
-  __syncthreads();
-  return r;
+  if (total) *total = all;
+  __syncthreads();  // wsum may be reused right away
+  return before + x - v;
 }
 
 struct SelShared {
@@ -202,9 +196,9 @@ struct SelShared {
 };
 
 // Finds, over `nbins` counters hist[0..nbins) (bin nbins-1 highest), the bin holding the need-th
-// largest key.  Each thread covers nbins / kSelThreads consecutive bins, highest bins on thread 0.
-// Returns the total count.
-template <int PER>
+// largest key.  Each of the NW * 64 threads covers PER = nbins / (NW * 64) consecutive bins,
+// highest bins on thread 0.  Returns the total count.
+template <int PER, int NW = kSelWaves>
 __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t need, SelShared& sh) {
   uint32_t cnt[PER];
   uint32_t sum = 0;
@@ -216,7 +210,7 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
   }
   if (threadIdx.x == 0) sh.found = 0u;
   uint32_t total;
-  uint32_t above = block_excl_scan(sum, sh.wsum, &total);
+  uint32_t above = block_excl_scan<NW>(sum, sh.wsum, &total);
   if (above < need && above + sum >= need) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -234,9 +228,69 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
   return total;
 }
 
-// Per row (b, t, hq): select the kk = min(k_b, visible) largest scores.
-//  1. threshold bin T12 of the 12-bit key prefix from the fused histogram (rebuilt from the scores
-//     when it does not add up to the visible count);
+// Shared memory of the select kernels (dynamic part; the layout select_lds_bytes sizes).
+struct SelLds {
+  uint32_t* hist;      // kHistBins
+  uint32_t* gt_bits;   // bitmap words: positions taken
+  uint32_t* eq_bits;   // bitmap words: positions whose key equals the k-th key
+  uint32_t* cand_key;  // kCandCap
+  uint32_t* cand_pos;  // kCandCap
+};
+
+__device__ __forceinline__ SelLds sel_lds(uint32_t* smem, int bitmap_words) {
+  SelLds l;
+  l.hist = smem;
+  l.gt_bits = l.hist + kHistBins;
+  l.eq_bits = l.gt_bits + bitmap_words;
+  l.cand_key = l.eq_bits + bitmap_words;
+  l.cand_pos = l.cand_key + kCandCap;
+  return l;
+}
+
+// Keeps the `need` lowest positions flagged in eq_bits (keys equal to the k-th key) unless all of
+// them are taken, then writes the positions flagged in gt_bits in ascending order (kk of them)
+// and pads the row to k_max with -1.  The caller synchronises before.
+__device__ void emit_selection(const SelLds& l, int words, uint32_t need, bool take_all_eq, int kk,
+                               int k_max, int32_t* __restrict__ out, SelShared& sh) {
+  const int tid = threadIdx.x;
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;  // bitmap words per thread
+  const int w0 = tid * wpt;
+  if (!take_all_eq) {
+    // keep the `need` lowest positions among keys equal to K*
+    uint32_t cnt = 0;
+    for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(l.eq_bits[w]);
+    uint32_t before = block_excl_scan(cnt, sh.wsum, nullptr);
+    for (int w = w0; w < min(w0 + wpt, words); ++w) {
+      uint32_t bits = l.eq_bits[w];
+      while (bits) {
+        const uint32_t bit = bits & (0u - bits);
+        if (before < need) l.gt_bits[w] |= bit;
+        ++before;
+        bits ^= bit;
+      }
+    }
+    __syncthreads();
+  }
+
+  uint32_t cnt = 0;
+  for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(l.gt_bits[w]);
+  uint32_t pos = block_excl_scan(cnt, sh.wsum, nullptr);
+  for (int w = w0; w < min(w0 + wpt, words); ++w) {
+    uint32_t bits = l.gt_bits[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      if (pos < (uint32_t)k_max) out[pos] = w * 32 + bit;
+      ++pos;
+      bits &= bits - 1;
+    }
+  }
+  for (int i = kk + tid; i < k_max; i += kSelThreads) out[i] = -1;
+}
+
+// Selects the kk largest of srow[0, vis) (1 <= kk < vis) into out, ascending, padded to k_max
+// with -1.  hist_row is the row's 12-bit key-prefix histogram, or nullptr to build it here.
+//  1. threshold bin T12 of the 12-bit prefix from the histogram (rebuilt from the scores when it
+//     does not add up to the visible count);
 //  2. one pass over the scores (16-byte loads): keys above T12 are marked in an LDS bitmap (8
 //     lanes' 4-bit nibbles OR-reduced per 32-bit word), keys in T12 are appended to an LDS
 //     candidate list;
@@ -244,36 +298,16 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
 //     equal to K* are taken (lowest positions first); when T12 holds more than kCandCap keys the
 //     rounds read the scores instead;
 //  4. the bitmap is emitted in ascending position order by a block prefix sum of popcounts.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_req, int T, int Hq,
-    int max_len, int64_t score_stride, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
-  extern __shared__ uint32_t smem[];
-  uint32_t* hist_s = smem;                      // kHistBins
-  uint32_t* gt_bits = hist_s + kHistBins;       // bitmap_words
-  uint32_t* eq_bits = gt_bits + bitmap_words;   // bitmap_words
-  uint32_t* cand_key = eq_bits + bitmap_words;  // kCandCap
-  uint32_t* cand_pos = cand_key + kCandCap;     // kCandCap
-  __shared__ SelShared sh;
-
-  const int row = blockIdx.x;
-  const int b = row / (T * Hq);
-  const int t = (row / Hq) - (row / (T * Hq)) * T;
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_len ? max_len : L);
-  const int vis = max(0, L - T + t + 1);
-  int kb = k_per_req ? k_per_req[b] : k_max;
-  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
-  const int kk = min(kb, vis);
-  int32_t* out = indices + (int64_t)row * k_max;
-  const float* srow = scores + (int64_t)row * score_stride;
+__device__ void select_dense_row(const float* __restrict__ srow, const uint32_t* __restrict__ hist_row,
+                                 int vis, int kk, int k_max, int32_t* __restrict__ out,
+                                 const SelLds& l, SelShared& sh) {
+  uint32_t* hist_s = l.hist;
+  uint32_t* gt_bits = l.gt_bits;
+  uint32_t* eq_bits = l.eq_bits;
+  uint32_t* cand_key = l.cand_key;
+  uint32_t* cand_pos = l.cand_pos;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-
-  if (kk == vis) {  // everything visible is selected (also kk == 0)
-    for (int i = tid; i < k_max; i += kSelThreads) out[i] = i < vis ? i : -1;
-    return;
-  }
 
   const int words = ((vis + 255) >> 8) * 8;  // bitmap words touched (256-position granules)
   for (int i = tid; i < words; i += kSelThreads) {
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   constexpr int kSelIter = kSelThreads * 4 * kSelVecUnroll;
   // the row's histogram: one 16-byte load per thread, issued first
   static_assert(kHistBins == 4 * kSelThreads, "one uint4 of histogram bins per thread");
-  const uint4 hv = reinterpret_cast<const uint4*>(hist + (int64_t)row * kHistBins)[tid];
+  const uint4 hv = hist_row ? reinterpret_cast<const uint4*>(hist_row)[tid] : make_uint4(0, 0, 0, 0);
   float4 sv[kSelVecUnroll];
   auto load_iter = [&](int B) {
 #pragma unroll
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   reinterpret_cast<uint4*>(hist_s)[tid] = hv;
   __syncthreads();
   uint32_t total = find_threshold<kHistBins / kSelThreads>(hist_s, kHistBins, (uint32_t)kk, sh);
-  if (total != (uint32_t)vis || !sh.found) {
+  if (!hist_row || total != (uint32_t)vis || !sh.found) {
     // histogram does not describe this row: rebuild it from the scores
     for (int i = tid; i < kHistBins; i += kSelThreads) hist_s[i] = 0u;
     __syncthreads();
@@ -448,39 +482,588 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
   __syncthreads();
 
-  const int wpt = (words + kSelThreads - 1) / kSelThreads;  // bitmap words per thread
-  const int w0 = tid * wpt;
-  if (!take_all_eq) {
-    // keep the `need` lowest positions among keys equal to K*
-    uint32_t cnt = 0;
-    for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(eq_bits[w]);
-    uint32_t before = block_excl_scan(cnt, sh.wsum, nullptr);
-    for (int w = w0; w < min(w0 + wpt, words); ++w) {
-      uint32_t bits = eq_bits[w];
-      while (bits) {
-        const uint32_t bit = bits & (0u - bits);
-        if (before < need) gt_bits[w] |= bit;
-        ++before;
-        bits ^= bit;
-      }
+  emit_selection(l, words, need, take_all_eq, kk, k_max, out, sh);
+}
+
+// One workgroup per row (b, t, hq): the kk = min(k_b, visible) largest scores of the row, from
+// the scores and histogram of score_hist_kernel.
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_req, int T, int Hq,
+    int max_len, int64_t score_stride, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
+  extern __shared__ uint32_t smem[];
+  __shared__ SelShared sh;
+  const int row = blockIdx.x;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > max_len ? max_len : L);
+  const int vis = max(0, L - T + t + 1);
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, vis);
+  int32_t* out = indices + (int64_t)row * k_max;
+  if (kk == vis || kk == 0) {  // everything visible is selected, or nothing
+    for (int i = threadIdx.x; i < k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
+    return;
+  }
+  select_dense_row(scores + (int64_t)row * score_stride, hist + (int64_t)row * kHistBins, vis, kk,
+                   k_max, out, sel_lds(smem, bitmap_words), sh);
+}
+
+// ============================================================================ filtered indexer
+// Writing every fp32 score and reading it back costs more than the 4 or 16 bytes per position
+// suggest (the writes interleave with the K stream), so for k <= N/16 the indexer avoids them:
+//  A. sample_keys_kernel scores a strided sample of at most kTauSamples positions per (request,
+//     KV head) and stores the ordered keys of each row's samples;
+//  B. score_cand_kernel first sets, per row, a threshold tau: the 16-bit key prefix of the
+//     sample's r-th largest score, r ~ kCandFactor * k * (samples / visible).  It then scores
+//     every position once, as score_hist_kernel does, and keeps only the candidates s >= tau as
+//     (position, score) pairs, staged in LDS and written a 128-byte line at a time into per-wave
+//     slots of the workspace.  A wave scans one contiguous range, so the slots concatenated in
+//     (chunk, wave) order list a row's candidates in ascending position order;
+//  C. cand_select_kernel selects the k largest candidates by radix select and writes them in that
+//     order.  They are the exact top-k whenever there are at least k candidates (then the k-th
+//     largest score is >= tau, so every position of the top-k is a candidate) and no slot
+//     overflowed; otherwise the workgroup recomputes every score of its row and selects from
+//     those (exact, slow, rare).
+constexpr int kTauSamples = 1024;
+constexpr int kCandFactor = 3;
+constexpr int kTauParts = 4;                                       // workgroups per (request, KV head, row tile)
+constexpr int kTauWaves = 4;
+constexpr int kTauTilesPerWave = kTauSamples / kTauParts / 16 / kTauWaves;  // 4
+static_assert(kTauTilesPerWave * 16 * kTauWaves * kTauParts == kTauSamples, "sample tiling");
+
+// Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
+__device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L + kTauSamples - 1) / kTauSamples : 1; }
+
+// Ordered key of a sampled score; 0 marks "not a sample of this row" (every finite score has a
+// larger key).
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kTauWaves * kWave) void sample_keys_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    uint32_t* __restrict__ keys) {
+  constexpr int KS = D / 32;
+  const int bh = blockIdx.x;
+  const int mt = blockIdx.y;
+  const int part = blockIdx.z;
+  const int Hkv = kv.num_kv_heads;
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int GT = G * T;
+  const int r0 = mt * 16;
+  const int rows_here = min(16, GT - r0);
+  const int L = seq_len_of(kv, b);
+  const int stride = tau_stride(L);
+  const int ns = (L + stride - 1) / stride;  // samples j * stride < L
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+
+  bf16x8 a[KS];
+  {
+    const int r = r0 + m;
+    if (r < GT) {
+      const int t = r / G, gi = r - (r / G) * G;
+      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     }
-    __syncthreads();
+  }
+  // sample j = part * 256 + 16 * (wave * kTauTilesPerWave + u) + m at position j * stride
+  // (loads clamped to the last sample)
+  const int j0 = part * (kTauSamples / kTauParts) + 16 * wave * kTauTilesPerWave;
+  uint4 kt[kTauTilesPerWave][KS];
+  const int jlast = max(ns - 1, 0);
+#pragma unroll
+  for (int u = 0; u < kTauTilesPerWave; ++u) {
+    const int j = min(j0 + 16 * u + m, jlast);
+    if (L > 0) {
+      const int64_t off = kv_row<D, PAGED>(kv, b, h, j * stride) + g4 * 8;
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) kt[u][kq] = ld16(kv.k + off + kq * 32);
+    } else {
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) kt[u][kq] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  int vis_i[4];
+  uint32_t* krow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * g4 + i;
+    const int r = r0 + rl;
+    const int t = r / G, gi = r - (r / G) * G;
+    vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
+    krow[i] = keys + (rl < rows_here ? (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples : 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kTauTilesPerWave; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kq], __builtin_bit_cast(bf16x8, kt[u][kq]), acc, 0, 0, 0);
+    const int j = j0 + 16 * u + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = j < ns && j * stride < vis_i[i];
+      if (4 * g4 + i < rows_here) krow[i][j] = ok ? max(ord_key(acc[i] * scale), 1u) : 0u;
+    }
+  }
+}
+
+// Candidate slots: wave w of workgroup (chunk c) of row `row` scans the positions
+// [c * chunk + w * chunk / kCandWaves, + chunk / kCandWaves) and owns slot s = c * kCandWaves + w
+// of the row's workspace area: up to cand_cap(chunk) (position, score) pairs, stored as 16-pair
+// lines interleaved across the row's nsub = chunks * kCandWaves slots -- line l of slot s is line
+// l * nsub + s of the area -- so the first lines of all slots, the ones most written, lie together.
+constexpr int kCandWaves = 4;
+__host__ __device__ constexpr int cand_cap(int chunk) { return chunk / (2 * kCandWaves); }
+
+// tau of one row from its sample keys (one wave): the largest 16-bit prefix P with at least r
+// keys >= P << 16, r = ceil(kCandFactor * kk * samples_visible / vis); -inf when every visible
+// position has to be a candidate, +inf when the selection needs none (k = 0 or k >= visible).
+__device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int stride) {
+  const int lane = threadIdx.x & 63;
+  if (kk <= 0 || kk >= vis) return INFINITY;
+  const int ns_row = (vis + stride - 1) / stride;
+  const int64_t rr = ((int64_t)kCandFactor * kk * ns_row + vis - 1) / vis;
+  if (rr >= ns_row) return -INFINITY;
+  uint32_t k16[kTauSamples / kWave];
+#pragma unroll
+  for (int e = 0; e < kTauSamples / kWave / 4; ++e) {
+    const uint4 v = reinterpret_cast<const uint4*>(krow)[e * kWave + lane];
+    k16[4 * e] = v.x >> 16;
+    k16[4 * e + 1] = v.y >> 16;
+    k16[4 * e + 2] = v.z >> 16;
+    k16[4 * e + 3] = v.w >> 16;
+  }
+  uint32_t P = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = P | (1u << bit);
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < kTauSamples / kWave; ++e) c += k16[e] >= cand ? 1u : 0u;
+    if (wave_sum_u32(c) >= (uint32_t)rr) P = cand;
+  }
+  return key_to_float(P << 16);
+}
+
+// Row mapping of the candidate pass: query row r of a 16-row tile sits in MFMA row
+// 4 * (r % 4) + r / 4, so lane group g4 (lanes 16 g4 .. 16 g4 + 15) holds rows 4 i + g4 for
+// i = 0..3 and, with 4 or 8 query rows, every lane group holds valid rows for the same i.
+template <int D, bool PAGED, int NI>
+__global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    const int32_t* __restrict__ k_per_req, int k_max, const uint32_t* __restrict__ sample_keys,
+    float* __restrict__ region, int64_t score_stride, uint32_t* __restrict__ counts, int chunk,
+    int chunks) {
+  extern __shared__ int lds_pages[];
+  __shared__ uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
+  __shared__ float th_s[16];
+  constexpr int KS = D / 32;
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int mt = blockIdx.z;
+  const int Hkv = kv.num_kv_heads;
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int GT = G * T;
+  const int r0 = mt * 16;
+  const int rows_here = min(16, GT - r0);
+  const int L = seq_len_of(kv, b);
+  const int start = c * chunk;
+  if (start >= L) return;
+  const int end = min(start + chunk, L);
+  if constexpr (PAGED) stage_pages(kv, b, start, end, lds_pages);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+  const int cap = cand_cap(chunk);
+  const int span = chunk / kCandWaves;
+  const int wbeg = start + wave * span;
+  const int wend = min(wbeg + span, end);
+
+  // thresholds of the workgroup's rows, one wave per row
+  {
+    int kb = k_per_req ? k_per_req[b] : k_max;
+    kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+    const int stride = tau_stride(L);
+    for (int rl = wave; rl < rows_here; rl += kCandWaves) {
+      const int r = r0 + rl;
+      const int t = r / G, gi = r - (r / G) * G;
+      const int vis = L - T + t + 1;
+      const float th = row_tau(sample_keys + (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples,
+                               vis, min(kb, max(vis, 0)), stride);
+      if (lane == 0) th_s[rl] = th;
+    }
   }
 
-  // ---- 4. emit ascending positions
-  uint32_t cnt = 0;
-  for (int w = w0; w < min(w0 + wpt, words); ++w) cnt += __popc(gt_bits[w]);
-  uint32_t pos = block_excl_scan(cnt, sh.wsum, nullptr);
-  for (int w = w0; w < min(w0 + wpt, words); ++w) {
-    uint32_t bits = gt_bits[w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      if (pos < (uint32_t)k_max) out[pos] = w * 32 + bit;
-      ++pos;
-      bits &= bits - 1;
+  bf16x8 a[KS];
+  {
+    const int rl = 4 * (m & 3) + (m >> 2);  // query row of MFMA row m
+    const int r = r0 + rl;
+    if (rl < rows_here) {
+      const int t = r / G, gi = r - (r / G) * G;
+      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     }
   }
-  for (int i = kk + tid; i < k_max; i += kSelThreads) out[i] = -1;
+  __syncthreads();  // page ids and thresholds
+  // Candidate lines are written with buffer stores through one resource spanning this
+  // workgroup's rows; a lane with nothing to write passes an offset past the resource, which
+  // the hardware drops.  Every tile thus issues the same stores with no branch around them, and
+  // the compiler keeps the K prefetch in flight across loop iterations.
+  int64_t row_lo, row_hi;
+  {
+    const int t0 = r0 / G, t1 = (r0 + rows_here - 1) / G;
+    row_lo = ((int64_t)b * T + t0) * Hq + (h * G + r0 - t0 * G);
+    row_hi = ((int64_t)b * T + t1) * Hq + (h * G + (r0 + rows_here - 1) - t1 * G);
+  }
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      region + row_lo * score_stride, (short)0, (int)((row_hi - row_lo + 1) * score_stride * 4), 0x00020000);
+  constexpr uint32_t kDrop = 0xfffffff0u;
+  const uint32_t line_stride = (uint32_t)chunks * kCandWaves * 128u;  // bytes from line l to l + 1 of a slot
+  // rows 4 i + g4 (i < NI = ceil(rows / 4), fixed at compile time) of this lane: visibility,
+  // threshold, byte offset of the slot; ring head, staged count, written count
+  int vis[4];
+  float th[4];
+  uint32_t slot[4];
+  int64_t grow[4];
+  bool valid[4];
+  uint32_t head[4] = {0u, 0u, 0u, 0u}, fill[4] = {0u, 0u, 0u, 0u}, done[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * i + g4;
+    const int r = r0 + rl;
+    valid[i] = rl < rows_here;
+    if (valid[i]) {
+      const int t = r / G, gi = r - (r / G) * G;
+      grow[i] = ((int64_t)b * T + t) * Hq + (h * G + gi);
+      vis[i] = L - T + t + 1;
+      th[i] = th_s[rl];
+    } else {
+      grow[i] = 0;
+      vis[i] = 0;
+      th[i] = INFINITY;
+    }
+    slot[i] = (uint32_t)(((valid[i] ? grow[i] - row_lo : 0) * score_stride) * 4 +
+                         (int64_t)(c * kCandWaves + wave) * 128);
+  }
+
+  // kScoreUnroll adjacent 16-position tiles per iteration; the next iteration's K loads while
+  // this one is scored (ping-pong, unconditional loads clamped to the range's last tile)
+  constexpr int kStep = 16 * kScoreUnroll;
+  const int last = wend > wbeg ? (wend - 1) & ~15 : wbeg;
+  uint4 cur[kScoreUnroll][KS], nxt[kScoreUnroll][KS];
+  auto load_tiles = [&](int n0, uint4 (&dst)[kScoreUnroll][KS]) {
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tile = min(n0 + u * 16, last);
+      const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
+                          (int64_t)min(m, L - 1 - tile) * D + g4 * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) dst[u][j] = ld16(kv.k + off + j * 32);
+    }
+  };
+  // Per tile and row: candidates s >= tau join the row's 32-entry LDS ring; once it holds 16, the
+  // 16 from its head are written as one 128-byte line.
+  // Tiles past the range (the second of a pair at the end) are scored on reloaded data and
+  // keep nothing, so every iteration runs the same instructions.
+  auto score_tiles = [&](int n0, const uint4 (&kt)[kScoreUnroll][KS]) {
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tile = n0 + u * 16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kt[u][j]),
+                                                      acc, 0, 0, 0);
+      const int n = tile + m;
+      const bool in_range = n < wend;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint2* st = stage[wave][4 * i + g4];
+        const float s = acc[i] * scale;
+        const bool pred = in_range && n < vis[i] && s >= th[i];
+        const uint64_t mask = __ballot(pred);
+        const uint32_t seg = (uint32_t)(mask >> (16 * g4)) & 0xffffu;
+        if (pred) st[(head[i] + fill[i] + __popc(seg & ((1u << m) - 1u))) & 31u] =
+            make_uint2((uint32_t)n, __float_as_uint(s));
+        fill[i] += __popc(seg);
+        wave_lds_fence();
+        const uint2 v = st[(head[i] + m) & 31u];
+        const bool full = fill[i] >= 16u;
+        const bool write = full && valid[i] && done[i] + 16u <= (uint32_t)cap;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
+                                              (int)(write ? slot[i] + (done[i] / 16u) * line_stride + m * 8u : kDrop), 0, 0);
+        head[i] = full ? (head[i] + 16u) & 31u : head[i];
+        done[i] += full ? 16u : 0u;
+        fill[i] -= full ? 16u : 0u;
+      }
+    }
+  };
+  if (wbeg < wend) {
+    int n0 = wbeg;
+    load_tiles(n0, cur);
+    do {
+      load_tiles(n0 + kStep, nxt);
+      score_tiles(n0, cur);
+      load_tiles(n0 + 2 * kStep, cur);
+      score_tiles(n0 + kStep, nxt);
+      n0 += 2 * kStep;
+    } while (n0 < wend);
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint2 v = stage[wave][4 * i + g4][(head[i] + m) & 31u];
+    const bool write = valid[i] && (uint32_t)m < fill[i] && done[i] + m < (uint32_t)cap;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
+                                          (int)(write ? slot[i] + ((done[i] + m) / 16u) * line_stride + ((done[i] + m) & 15u) * 8u : kDrop), 0, 0);
+    if (valid[i] && m == 0) counts[(grow[i] * chunks + c) * kCandWaves + wave] = done[i] + fill[i];
+  }
+}
+
+// ---- C: selection over a position-ordered list of (position, key) items
+constexpr int kCsThreads = 256;
+constexpr int kCsWaves = kCsThreads / kWave;
+constexpr int kMaxCandSlots = (262144 / 1024) * kCandWaves;  // chunks of >= 1024 positions
+constexpr int kCsPer = 8;  // consecutive items per thread in the ordered passes
+
+// Candidates of a row in position order, from the slots: item f lives in the slot s with
+// prefix[s] <= f < prefix[s + 1].  Keys come from LDS when lds_key is set.
+struct CandSource {
+  const uint2* base;       // the row's slot area
+  const uint32_t* prefix;  // [nsub + 1] exclusive prefix of the slot counts (LDS)
+  int nsub, cap;
+  int nsub_all;            // slots of a row (chunks * kCandWaves): the line interleave
+  const uint32_t* lds_key;
+  // pair index of entry j of slot sl (16-pair lines interleaved across the nsub_all slots)
+  __device__ __forceinline__ int64_t pair_of(int sl, int j) const {
+    return ((int64_t)(j >> 4) * nsub_all + sl) * 16 + (j & 15);
+  }
+  __device__ __forceinline__ int slot_of(int f) const {
+    int lo = 0, hi = nsub - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)prefix[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  // pair offsets of items f0 .. f0 + kCsPer - 1 (the valid ones, f < total)
+  __device__ __forceinline__ void offsets(int f0, int total, int64_t (&off)[kCsPer]) const {
+    int sl = f0 < total ? slot_of(f0) : 0;
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) {
+      const int f = f0 + e;
+      if (f < total) {
+        while ((int)prefix[sl + 1] <= f) ++sl;
+        off[e] = pair_of(sl, f - (int)prefix[sl]);
+      } else {
+        off[e] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ uint32_t key(int f) const {
+    if (lds_key) return lds_key[f];
+    const int sl = slot_of(f);
+    return ord_key(__uint_as_float(base[pair_of(sl, f - (int)prefix[sl])].y));
+  }
+  __device__ __forceinline__ void pos8(int f0, int total, uint32_t sel, uint32_t (&p)[kCsPer]) const {
+    int64_t off[kCsPer];
+    offsets(f0, total, off);
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) p[e] = ((sel >> e) & 1u) ? base[off[e]].x : 0u;
+  }
+};
+
+// Every score of a row (the exact fallback), position = index.
+struct DenseSource {
+  const float* s;
+  __device__ __forceinline__ uint32_t key(int f) const { return ord_key(s[f]); }
+  __device__ __forceinline__ void pos8(int f0, int, uint32_t, uint32_t (&p)[kCsPer]) const {
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) p[e] = (uint32_t)(f0 + e);
+  }
+};
+
+// Writes, in list order, the kk items of the largest keys (ties at the k-th key: earliest items)
+// and pads out to k_max with -1.  Radix select in rounds of 11, 11 and 10 bits over the list;
+// hist holds 2048 counters.
+template <class Src>
+__device__ void select_ordered(const Src& src, int total, int kk, int k_max, int32_t* __restrict__ out,
+                               uint32_t* hist, SelShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, need = (uint32_t)kk, cnt_eq = 0;
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kWidth[3] = {11, 11, 10};
+#pragma unroll
+  for (int round = 0; round < 3; ++round) {
+    const int shift = kShift[round], nb = 1 << kWidth[round];
+    for (int i = tid; i < nb; i += kCsThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int f = tid; f < total; f += kCsThreads) {
+      const uint32_t key = src.key(f);
+      if (round == 0 || (key >> (shift + kWidth[round])) == prefix)
+        atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (round < 2)
+      find_threshold<2048 / kCsThreads, kCsWaves>(hist, nb, need, sh);
+    else
+      find_threshold<1024 / kCsThreads, kCsWaves>(hist, nb, need, sh);
+    prefix = (prefix << kWidth[round]) | sh.thr_bin;
+    need -= sh.thr_above;
+    cnt_eq = sh.thr_count;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;  // the kk-th largest key
+  const bool take_all_eq = cnt_eq == need;
+  uint32_t eq_base = 0, out_base = 0;
+  for (int f0 = 0; f0 < total; f0 += kCsThreads * kCsPer) {
+    const int fb = f0 + tid * kCsPer;
+    uint32_t keys[kCsPer];
+    uint32_t eqc = 0;
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) {
+      keys[e] = fb + e < total ? src.key(fb + e) : 0u;
+      eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
+    }
+    uint32_t eq_tot, sel_tot;
+    uint32_t eq_rank = eq_base + block_excl_scan<kCsWaves>(eqc, sh.wsum, &eq_tot);
+    uint32_t selc = 0, selm = 0;
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) {
+      if (fb + e >= total) continue;
+      bool sel = keys[e] > kstar;
+      if (keys[e] == kstar) {
+        sel = take_all_eq || eq_rank < need;
+        ++eq_rank;
+      }
+      selm |= (uint32_t)sel << e;
+      selc += sel ? 1u : 0u;
+    }
+    uint32_t o = out_base + block_excl_scan<kCsWaves>(selc, sh.wsum, &sel_tot);
+    uint32_t p[kCsPer];
+    src.pos8(fb, total, selm, p);
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e)
+      if ((selm >> e) & 1u) out[o++] = (int32_t)p[e];
+    eq_base += eq_tot;
+    out_base += sel_tot;
+  }
+  for (int i = kk + tid; i < k_max; i += kCsThreads) out[i] = -1;
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
+    const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int lds_cap,
+    int32_t* __restrict__ indices) {
+  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
+  __shared__ SelShared sh;
+  __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
+  uint32_t* lds_key = smem;
+  uint32_t* hist = smem + lds_cap;
+  const int row = blockIdx.x;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  const int hq = row - (row / Hq) * Hq;
+  const int L = seq_len_of(kv, b);
+  const int vis = max(0, L - T + t + 1);
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, vis);
+  int32_t* out = indices + (int64_t)row * k_max;
+  const int tid = threadIdx.x;
+  if (kk == vis || kk == 0) {  // everything visible is selected, or nothing
+    for (int i = tid; i < k_max; i += kCsThreads) out[i] = i < kk ? i : -1;
+    return;
+  }
+
+  // ---- slot counts of the chunks holding positions < L, and their prefix sums
+  const int cap = cand_cap(chunk);
+  const int nsub = ((L + chunk - 1) / chunk) * kCandWaves;
+  constexpr int kPerT = kMaxCandSlots / kCsThreads;  // slots per thread
+  uint32_t cc[kPerT];
+  uint32_t local = 0;
+  bool over = false;
+#pragma unroll
+  for (int e = 0; e < kPerT; ++e) {
+    const int sidx = tid * kPerT + e;
+    const uint32_t cnt = sidx < nsub ? counts[(int64_t)row * chunks * kCandWaves + sidx] : 0u;
+    over |= cnt > (uint32_t)cap;
+    cc[e] = cnt > (uint32_t)cap ? (uint32_t)cap : cnt;
+    local += cc[e];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan<kCsWaves>(local, sh.wsum, &total);
+#pragma unroll
+  for (int e = 0; e < kPerT; ++e) {
+    prefix_s[tid * kPerT + e] = run;
+    run += cc[e];
+  }
+  if (tid == 0) prefix_s[kMaxCandSlots] = total;
+  const bool overflow = __syncthreads_or(over) != 0;
+
+  if (overflow || total < (uint32_t)kk) {
+    // ---- exact fallback: every score of the row into its workspace area, then select
+    float* srow = region + (int64_t)row * score_stride;
+    constexpr int LPP = D / 8, PPW = kWave / LPP;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int p = lane / LPP, cdim = lane - (lane / LPP) * LPP;
+    const int h = hq / G;
+    const uint4 qv = ld16(q + (int64_t)row * D + cdim * 8);
+    for (int n0 = wave * PPW; n0 < vis; n0 += kCsWaves * PPW) {
+      const int n = n0 + p;
+      const bool ok = n < vis;
+      const uint4 kr = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, ok ? n : 0) + cdim * 8);
+      float dot = 0.f;
+      dot = dot2_bf16(qv.x, kr.x, dot);
+      dot = dot2_bf16(qv.y, kr.y, dot);
+      dot = dot2_bf16(qv.z, kr.z, dot);
+      dot = dot2_bf16(qv.w, kr.w, dot);
+      dot = group_sum<LPP>(dot);
+      if (ok && cdim == 0) srow[n] = dot * scale;
+    }
+    __syncthreads();
+    select_ordered(DenseSource{srow}, vis, kk, k_max, out, hist, sh);
+    return;
+  }
+
+  CandSource src;
+  src.base = reinterpret_cast<const uint2*>(region + (int64_t)row * score_stride);
+  src.prefix = prefix_s;
+  src.nsub = nsub;
+  src.cap = cap;
+  src.nsub_all = chunks * kCandWaves;
+  src.lds_key = nullptr;
+  if (total <= (uint32_t)lds_cap) {
+    // keys into LDS once, kCsPer consecutive items per thread with their loads in flight together
+    for (int f0 = tid * kCsPer; f0 < (int)total; f0 += kCsThreads * kCsPer) {
+      int64_t off[kCsPer];
+      src.offsets(f0, (int)total, off);
+      uint32_t bits[kCsPer];
+#pragma unroll
+      for (int e = 0; e < kCsPer; ++e) bits[e] = src.base[off[e]].y;
+#pragma unroll
+      for (int e = 0; e < kCsPer; ++e)
+        if (f0 + e < (int)total) lds_key[f0 + e] = ord_key(__uint_as_float(bits[e]));
+    }
+    __syncthreads();
+    src.lds_key = lds_key;
+  }
+  select_ordered(src, (int)total, kk, k_max, out, hist, sh);
 }
 
 // ============================================================================ launchers
@@ -519,7 +1102,44 @@ static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool PAGED>
+static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
+  const int tiles = (a.GT + 15) / 16;
+  const int groups = a.B * a.kv.num_kv_heads;
+  hipLaunchKernelGGL((sample_keys_kernel<D, PAGED>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
+                     0, stream, a.q, a.kv, a.T, a.Hq, a.G, a.scale, a.sample_keys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
+  const int rows_tile = a.GT < 16 ? a.GT : 16;
+  auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1>
+                             : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2> : score_cand_kernel<D, PAGED, 4>);
+  hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
+                     page_ids * sizeof(int), stream, a.q, a.kv, a.T, a.Hq, a.G, a.scale, a.k_per_req,
+                     a.k_max, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                     a.cand_chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // candidate keys held in LDS: about kCandFactor * k expected, room for 4.5 k (at most 12288)
+  int lds_cap = (int)(((int64_t)a.k_max * 9 / 2 + 255) / 256 * 256);
+  if (lds_cap > 12288) lds_cap = 12288;
+  const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
+  auto sel = cand_select_kernel<D, PAGED>;
+  if (lds > 65536) {
+    e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
+                     a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                     a.cand_chunks, a.k_max, lds_cap, a.indices);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
+  if (a.filtered) {
+    if (a.D == 128)
+      return a.paged ? launch_filtered_t<128, true>(a, stream) : launch_filtered_t<128, false>(a, stream);
+    return a.paged ? launch_filtered_t<64, true>(a, stream) : launch_filtered_t<64, false>(a, stream);
+  }
   hipError_t e = launch_fill_u32(a.hist, (int64_t)a.rows * kHistBins, 0u, stream);
   if (e != hipSuccess) return e;
   if (a.D == 128)

@@ -1,0 +1,90 @@
+"""GPU parity of the indexer's two paths against the CPU oracle.
+
+For k <= max_len / 16 the indexer first estimates a per-row score threshold from a strided sample
+of at most 1024 positions per (request, KV head), keeps only the positions scoring at or above it
+as candidates and selects among those; when fewer than k candidates survive (or a candidate slot
+overflows) the row is recomputed in full.  Larger k use the full-score path directly.  These
+tests drive each branch, the boundary between the paths and per-request k including 0 and
+k >= visible.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._util import bits, oracle_cache
+from tests.gpu_util import all_rows, cache_of, check_topk_row
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import long_context_sparse_oracle_amd as m
+
+    return m
+
+
+def _check_indexer(wl_cpu, k_max=None):
+    m = _lib()
+    wl = wl_cpu.to("cuda")
+    kmax = wl.k_max if k_max is None else k_max
+    idx = m.topk_index(wl.q, cache_of(wl), wl.k_per_req, k_max=kmax)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    q = oracle.bf16_bits_to_f64(bits(wl_cpu.q))
+    ocache = oracle_cache(wl_cpu)
+    kreq = wl_cpu.k_per_req.numpy()
+    for b, t, hq in all_rows(wl_cpu):
+        K = ocache.keys(b, hq // wl.group)
+        vis = oracle.visible_length(ocache.seq_lens[b], wl.q_len, t)
+        check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, min(int(kreq[b]), kmax), f"row {(b, t, hq)}")
+    return idx
+
+
+def test_threshold_from_unrepresentative_sample_falls_back():
+    """The sampled positions (every 32nd of 32768) hold 100 planted keys that score about 3, far
+    above everything else, so the sampled threshold leaves fewer than k = 655 candidates: the
+    rows must be recomputed in full and still give the exact top-k."""
+    L, k = 32768, 655
+    wl = make_workload(batch=1, q_len=1, num_q_heads=2, num_kv_heads=2, head_dim=128,
+                       seq_lens=[L], k=k, seed=41)
+    for h in range(2):
+        qh = wl.q[0, 0, h].float()
+        key = (3.0 * qh / qh.norm()).to(torch.bfloat16)
+        wl.k_cache[0, h, torch.arange(100) * (L // 1024)] = key
+    idx = _check_indexer(wl)
+    for h in range(2):
+        planted = set((np.arange(100) * (L // 1024)).tolist())
+        assert planted <= set(idx[0, 0, h].tolist())
+
+
+def test_threshold_path_many_rows_gqa():
+    """Filtered path with GQA 8, several chunks per row and a ragged tail."""
+    wl = make_workload(batch=2, q_len=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                       seq_lens=[40000, 23457], k=0.02, max_len=40003, needles_per_head=4, seed=42)
+    _check_indexer(wl)
+
+
+@pytest.mark.parametrize("k,label", [(256, "filtered at k = N/16"), (257, "full-score path")])
+def test_path_boundary(k, label):
+    wl = make_workload(batch=2, q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                       seq_lens=[4096, 3000], k=k, max_len=4096, seed=43)
+    _check_indexer(wl)
+
+
+def test_per_request_k_zero_small_and_all():
+    # k_max 256 of max_len 4096 (filtered); request 0 asks for none, request 3 for more than it has
+    wl = make_workload(batch=4, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                       seq_lens=[4096, 1000, 3000, 200], k=[0, 5, 256, 256], max_len=4096, seed=44)
+    idx = _check_indexer(wl, k_max=256)
+    assert (idx[0] == -1).all()
+    assert idx[3, 0, :, :200].tolist() == [list(range(200))] * 4
+
+
+def test_paged_filtered_causal():
+    wl = make_workload(batch=3, q_len=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       seq_lens=[20000, 5000, 900], k=0.02, layout="paged", page_size=16,
+                       max_len=20480, needles_per_head=2, seed=45)
+    _check_indexer(wl)
