@@ -188,6 +188,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 
 struct SelShared {
   uint32_t wsum[kSelWaves + 1];
+  uint32_t kmin, kmax;  // key range of a candidate list
   uint32_t cand_count;
   uint32_t thr_bin;    // bin holding the k-th largest key
   uint32_t thr_above;  // keys in higher bins
@@ -896,70 +897,93 @@ struct DenseSource {
   }
 };
 
+constexpr int kCsMaxBlocks = 6;  // candidate blocks of kCsThreads * kCsPer held with positions in registers
+
+// Finds the kk-th largest key of the list (kmin <= every key <= kmax) by radix select over the
+// bits below their common prefix, in digits of up to 11 bits; hist holds 2048 counters.
+// Returns the key and sets need (items equal to it that are taken) and cnt_eq (items equal to it).
+template <class KeyAt>
+__device__ uint32_t radix_kth(KeyAt key_at, int total, int kk, uint32_t kmin, uint32_t kmax,
+                              uint32_t* hist, SelShared& sh, uint32_t& need, uint32_t& cnt_eq) {
+  const int tid = threadIdx.x;
+  need = (uint32_t)kk;
+  cnt_eq = (uint32_t)total;
+  if (kmin == kmax) return kmin;  // one key value
+  int lo = 32 - __clz(kmin ^ kmax);  // bits [0, lo) vary
+  uint32_t prefix = lo >= 32 ? 0u : kmin >> lo;
+  while (lo > 0) {
+    const int width = lo >= 11 ? 11 : lo;
+    const int shift = lo - width;
+    const int nb = 1 << width;
+    for (int i = tid; i < nb; i += kCsThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int f = tid; f < total; f += kCsThreads) {
+      const uint32_t key = key_at(f);
+      if (lo >= 32 || (key >> lo) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    for (int i = nb + tid; i < 2048; i += kCsThreads) hist[i] = 0u;  // bins above nb count nothing
+    __syncthreads();
+    find_threshold<2048 / kCsThreads, kCsWaves>(hist, 2048, need, sh);
+    prefix = (prefix << width) | sh.thr_bin;
+    need -= sh.thr_above;
+    cnt_eq = sh.thr_count;
+    lo = shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Emission of one block of list items in list order: item fb + e (e < kCsPer) of this thread, key
+// keys[e], position pos[e]; selected are keys > kstar and the first `need` keys == kstar (unless
+// take_all_eq).  eq_base / out_base carry the counts of the earlier blocks.
+__device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&keys)[kCsPer],
+                                           const uint32_t (&pos)[kCsPer], uint32_t kstar, uint32_t need,
+                                           bool take_all_eq, uint32_t& eq_base, uint32_t& out_base,
+                                           int32_t* __restrict__ out, SelShared& sh) {
+  uint32_t eqc = 0;
+#pragma unroll
+  for (int e = 0; e < kCsPer; ++e) eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
+  uint32_t eq_tot, sel_tot;
+  uint32_t eq_rank = eq_base + block_excl_scan<kCsWaves>(eqc, sh.wsum, &eq_tot);
+  uint32_t selc = 0, selm = 0;
+#pragma unroll
+  for (int e = 0; e < kCsPer; ++e) {
+    if (fb + e >= total) continue;
+    bool sel = keys[e] > kstar;
+    if (keys[e] == kstar) {
+      sel = take_all_eq || eq_rank < need;
+      ++eq_rank;
+    }
+    selm |= (uint32_t)sel << e;
+    selc += sel ? 1u : 0u;
+  }
+  uint32_t o = out_base + block_excl_scan<kCsWaves>(selc, sh.wsum, &sel_tot);
+#pragma unroll
+  for (int e = 0; e < kCsPer; ++e)
+    if ((selm >> e) & 1u) out[o++] = (int32_t)pos[e];
+  eq_base += eq_tot;
+  out_base += sel_tot;
+}
+
 // Writes, in list order, the kk items of the largest keys (ties at the k-th key: earliest items)
-// and pads out to k_max with -1.  Radix select in rounds of 11, 11 and 10 bits over the list;
-// hist holds 2048 counters.
+// and pads out to k_max with -1.  Keys and positions come from src (list in global memory).
 template <class Src>
 __device__ void select_ordered(const Src& src, int total, int kk, int k_max, int32_t* __restrict__ out,
                                uint32_t* hist, SelShared& sh) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, need = (uint32_t)kk, cnt_eq = 0;
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kWidth[3] = {11, 11, 10};
-#pragma unroll
-  for (int round = 0; round < 3; ++round) {
-    const int shift = kShift[round], nb = 1 << kWidth[round];
-    for (int i = tid; i < nb; i += kCsThreads) hist[i] = 0u;
-    __syncthreads();
-    for (int f = tid; f < total; f += kCsThreads) {
-      const uint32_t key = src.key(f);
-      if (round == 0 || (key >> (shift + kWidth[round])) == prefix)
-        atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    if (round < 2)
-      find_threshold<2048 / kCsThreads, kCsWaves>(hist, nb, need, sh);
-    else
-      find_threshold<1024 / kCsThreads, kCsWaves>(hist, nb, need, sh);
-    prefix = (prefix << kWidth[round]) | sh.thr_bin;
-    need -= sh.thr_above;
-    cnt_eq = sh.thr_count;
-    __syncthreads();
-  }
-  const uint32_t kstar = prefix;  // the kk-th largest key
+  uint32_t need, cnt_eq;
+  const uint32_t kstar = radix_kth([&](int f) { return src.key(f); }, total, kk, 0u, 0xffffffffu, hist, sh,
+                                   need, cnt_eq);
   const bool take_all_eq = cnt_eq == need;
   uint32_t eq_base = 0, out_base = 0;
   for (int f0 = 0; f0 < total; f0 += kCsThreads * kCsPer) {
     const int fb = f0 + tid * kCsPer;
-    uint32_t keys[kCsPer];
-    uint32_t eqc = 0;
+    uint32_t keys[kCsPer], pos[kCsPer];
 #pragma unroll
-    for (int e = 0; e < kCsPer; ++e) {
-      keys[e] = fb + e < total ? src.key(fb + e) : 0u;
-      eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
-    }
-    uint32_t eq_tot, sel_tot;
-    uint32_t eq_rank = eq_base + block_excl_scan<kCsWaves>(eqc, sh.wsum, &eq_tot);
-    uint32_t selc = 0, selm = 0;
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e) {
-      if (fb + e >= total) continue;
-      bool sel = keys[e] > kstar;
-      if (keys[e] == kstar) {
-        sel = take_all_eq || eq_rank < need;
-        ++eq_rank;
-      }
-      selm |= (uint32_t)sel << e;
-      selc += sel ? 1u : 0u;
-    }
-    uint32_t o = out_base + block_excl_scan<kCsWaves>(selc, sh.wsum, &sel_tot);
-    uint32_t p[kCsPer];
-    src.pos8(fb, total, selm, p);
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e)
-      if ((selm >> e) & 1u) out[o++] = (int32_t)p[e];
-    eq_base += eq_tot;
-    out_base += sel_tot;
+    for (int e = 0; e < kCsPer; ++e) keys[e] = fb + e < total ? src.key(fb + e) : 0u;
+    src.pos8(fb, total, 0xffu, pos);
+    emit_block(fb, total, keys, pos, kstar, need, take_all_eq, eq_base, out_base, out, sh);
   }
   for (int i = kk + tid; i < k_max; i += kCsThreads) out[i] = -1;
 }
@@ -1048,22 +1072,57 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
   src.cap = cap;
   src.nsub_all = chunks * kCandWaves;
   src.lds_key = nullptr;
-  if (total <= (uint32_t)lds_cap) {
-    // keys into LDS once, kCsPer consecutive items per thread with their loads in flight together
-    for (int f0 = tid * kCsPer; f0 < (int)total; f0 += kCsThreads * kCsPer) {
-      int64_t off[kCsPer];
-      src.offsets(f0, (int)total, off);
-      uint32_t bits[kCsPer];
-#pragma unroll
-      for (int e = 0; e < kCsPer; ++e) bits[e] = src.base[off[e]].y;
-#pragma unroll
-      for (int e = 0; e < kCsPer; ++e)
-        if (f0 + e < (int)total) lds_key[f0 + e] = ord_key(__uint_as_float(bits[e]));
-    }
-    __syncthreads();
-    src.lds_key = lds_key;
+  if (total > (uint32_t)lds_cap) {  // too many to hold: every pass reads the slots
+    select_ordered(src, (int)total, kk, k_max, out, hist, sh);
+    return;
   }
-  select_ordered(src, (int)total, kk, k_max, out, hist, sh);
+  // keys into LDS and positions into registers, kCsPer consecutive items per thread and block
+  // (the same items the emission gives this thread), loads of a block in flight together
+  if (tid == 0) {
+    sh.kmin = 0xffffffffu;
+    sh.kmax = 0u;
+  }
+  __syncthreads();
+  uint32_t preg[kCsMaxBlocks][kCsPer];
+  uint32_t lmin = 0xffffffffu, lmax = 0u;
+#pragma unroll
+  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
+    if (blk * kCsThreads * kCsPer >= (int)total) break;
+    int64_t off[kCsPer];
+    src.offsets(fb, (int)total, off);
+    uint2 pr[kCsPer];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) pr[e] = src.base[off[e]];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) {
+      preg[blk][e] = pr[e].x;
+      if (fb + e < (int)total) {
+        const uint32_t key = ord_key(__uint_as_float(pr[e].y));
+        lds_key[fb + e] = key;
+        lmin = min(lmin, key);
+        lmax = max(lmax, key);
+      }
+    }
+  }
+  atomicMin(&sh.kmin, lmin);
+  atomicMax(&sh.kmax, lmax);
+  __syncthreads();
+  uint32_t need, cnt_eq;
+  const uint32_t kstar = radix_kth([&](int f) { return lds_key[f]; }, (int)total, kk, sh.kmin, sh.kmax,
+                                   hist, sh, need, cnt_eq);
+  const bool take_all_eq = cnt_eq == need;
+  uint32_t eq_base = 0, out_base = 0;
+#pragma unroll
+  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+    if (blk * kCsThreads * kCsPer >= (int)total) break;
+    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
+    uint32_t keys[kCsPer];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) keys[e] = fb + e < (int)total ? lds_key[fb + e] : 0u;
+    emit_block(fb, (int)total, keys, preg[blk], kstar, need, take_all_eq, eq_base, out_base, out, sh);
+  }
+  for (int i = kk + tid; i < k_max; i += kCsThreads) out[i] = -1;
 }
 
 // ============================================================================ launchers
@@ -1121,7 +1180,7 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // candidate keys held in LDS: about kCandFactor * k expected, room for 4.5 k (at most 12288)
   int lds_cap = (int)(((int64_t)a.k_max * 9 / 2 + 255) / 256 * 256);
-  if (lds_cap > 12288) lds_cap = 12288;
+  if (lds_cap > kCsMaxBlocks * kCsThreads * kCsPer) lds_cap = kCsMaxBlocks * kCsThreads * kCsPer;
   const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
   auto sel = cand_select_kernel<D, PAGED>;
   if (lds > 65536) {
