@@ -61,7 +61,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--sweep-k", default=None, help="k for the sweep workload (s10/s50/s100/s1000)")
+    p.add_argument("--sweep-k", default=None, help="k for a sweep workload (s10/s50/s100/s500/s1000)")
     p.add_argument("--sparse-splits", type=int, default=0)
     p.add_argument("--dense-splits", type=int, default=0)
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the reported figure)")
@@ -243,7 +243,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     overrides = {}
-    if args.workload == "sweep_b16_n128k" and args.sweep_k:
+    if args.workload.startswith("sweep_") and args.sweep_k:
         overrides["k"] = SWEEP_K[args.sweep_k]
     wl = make_named(args.workload, device=dev, **overrides)
     torch.cuda.synchronize()

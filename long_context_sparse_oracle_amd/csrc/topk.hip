@@ -625,13 +625,18 @@ constexpr int kCandWaves = 4;
 __host__ __device__ constexpr int cand_cap(int chunk) { return chunk / (2 * kCandWaves); }
 
 // tau of one row from its sample keys (one wave): the largest 16-bit prefix P with at least r
-// keys >= P << 16, r = ceil(kCandFactor * kk * samples_visible / vis); -inf when every visible
-// position has to be a candidate, +inf when the selection needs none (k = 0 or k >= visible).
+// keys >= P << 16, r = max(ceil(kCandFactor * kk * samples_visible / vis), kMinRank); -inf when
+// every visible position has to be a candidate, +inf when the selection needs none (k = 0 or
+// k >= visible).  The fraction of the row scoring >= tau then has mean about r / samples and
+// relative spread about 1 / sqrt(r); kMinRank keeps that spread small for very sparse k (where
+// the kCandFactor rule alone would put r at a handful of samples).
+constexpr int kMinRank = 32;
 __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int stride) {
   const int lane = threadIdx.x & 63;
   if (kk <= 0 || kk >= vis) return INFINITY;
   const int ns_row = (vis + stride - 1) / stride;
-  const int64_t rr = ((int64_t)kCandFactor * kk * ns_row + vis - 1) / vis;
+  int64_t rr = ((int64_t)kCandFactor * kk * ns_row + vis - 1) / vis;
+  if (rr < kMinRank) rr = kMinRank;
   if (rr >= ns_row) return -INFINITY;
   uint32_t k16[kTauSamples / kWave];
 #pragma unroll

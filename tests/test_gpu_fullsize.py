@@ -1,5 +1,5 @@
 """GPU parity at the named workloads' full sizes, in the launch configuration bench.py times
-(automatic splits and chunking).
+(automatic splits and chunking), including the sweep's 500x point and its 64-request batch.
 
 * Sampled rows (first, last and seeded random ones) are compared with the CPU oracle one by one:
   indexer by the band rule, sparse attention fed the oracle's own index lists, dense attention.
@@ -161,9 +161,17 @@ def sweep_wl():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("level", ["s10", "s50", "s100", "s1000"])
+@pytest.mark.parametrize("level", ["s10", "s50", "s100", "s500", "s1000"])
 def test_sweep_b16_n128k(sweep_wl, level):
     _run(sweep_wl, k=SWEEP_K[level], seed=13, check_dense=(level == "s50"))
+
+
+def test_sweep_b64_n128k_500x():
+    """The large-batch sweep point: 64 requests of 131072 positions, k = N/500."""
+    wl = make_named("sweep_b64_n128k", device="cuda")
+    _run(wl, seed=15)
+    del wl
+    torch.cuda.empty_cache()
 
 
 def test_ragged_paged_b32_t4():

@@ -291,10 +291,15 @@ NAMED = {
         k=2621, structure="lowrank", needles_per_head=0, seed=1003,
     ),
     # Sparsity sweep at fixed shape: 16 requests, GQA 32/8, d=128, N=131072; k is one of
-    # N/10, N/50, N/100, N/1000 (default N/50).
+    # N/10, N/50, N/100, N/500, N/1000 (default N/50).
     "sweep_b16_n128k": dict(
         batch=16, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=[131072] * 16,
         k=2621, structure="plain", needles_per_head=0, seed=1004,
+    ),
+    # The same sweep at a large batch: 64 requests (34 GB of K and V), default k = N/500.
+    "sweep_b64_n128k": dict(
+        batch=64, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=[131072] * 64,
+        k=262, structure="plain", needles_per_head=0, seed=1006,
     ),
     # Agentic ragged paged batch: 32 requests, L_b uniform in [8192, 131072], 4 query tokens,
     # GQA 32/8, d=128, page size 16 with a permuted page table, k_b = floor(0.02 * L_b),
@@ -306,7 +311,7 @@ NAMED = {
     ),
 }
 
-SWEEP_K = {"s10": 13107, "s50": 2621, "s100": 1310, "s1000": 131}
+SWEEP_K = {"s10": 13107, "s50": 2621, "s100": 1310, "s500": 262, "s1000": 131}
 
 
 def make_named(name: str, device="cpu", **overrides) -> Workload:
