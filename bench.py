@@ -5,6 +5,7 @@
 
 A step is one pass of the whole hot path over one decode batch, on one stream:
     flush -> topk_index -> flush -> sparse_decode_attn -> flush -> dense_decode_attn
+          -> flush -> sparse_decode_step (indexer + sparse attention in one call)
 `flush` reads a 2 GiB scratch buffer so that neither L2 nor the 256 MB Infinity Cache holds any
 KV bytes when a hot-path call starts (every call is measured from cold caches).  Each call is
 bracketed by HIP events recorded on the stream it runs on.  Inputs are seeded synthetic tensors
@@ -44,6 +45,9 @@ KERNEL_SOURCES = {
                           "long_context_sparse_oracle_amd/csrc/device_common.h"],
     "topk_index": ["long_context_sparse_oracle_amd/csrc/topk.hip",
                    "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "sparse_decode_step": ["long_context_sparse_oracle_amd/csrc/topk.hip",
+                           "long_context_sparse_oracle_amd/csrc/attention.hip",
+                           "long_context_sparse_oracle_amd/csrc/device_common.h"],
 }
 
 
@@ -97,6 +101,8 @@ def algorithmic_bytes(wl, idx):
         "selected_rows": nominal,
         "dense": 2 * tokens * Hkv * row_bytes + q_bytes + o_bytes,
         "topk": tokens * Hkv * row_bytes + index_bytes + q_bytes,
+        # the one-call step: all of K once (scores), V of the distinct selected rows, q, outputs
+        "step": tokens * Hkv * row_bytes + distinct * row_bytes + q_bytes + o_bytes,
     }
 
 
@@ -264,6 +270,10 @@ def main():
                        dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, cs.dense_decode_attn_workspace_size(wl.q, cache, args.dense_splits)),
                        dtype=torch.uint8, device=dev)
+    out_st = torch.empty_like(out_s)
+    lse_st = torch.empty_like(lse_s)
+    ws_st = torch.empty(max(1, cs.sparse_decode_step_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8,
+                        device=dev)
     # cache flush by reading 2 GiB: evicts every KV line from L2 and the Infinity Cache and leaves
     # clean lines behind (a write flush would leave dirty lines whose write-back the next call
     # would pay for)
@@ -281,6 +291,8 @@ def main():
                                                             out=out_s, lse=lse_s, workspace=ws_s),
         "dense_decode_attn": lambda: cs.dense_decode_attn(wl.q, cache, num_splits=args.dense_splits,
                                                           out=out_d, lse=lse_d, workspace=ws_d),
+        "sparse_decode_step": lambda: cs.sparse_decode_step(wl.q, cache, kptr, k_max=k_max, out=out_st,
+                                                            lse=lse_st, workspace=ws_st),
     }
     times = {k: [] for k in calls}
 
@@ -368,17 +380,20 @@ def main():
         "dense_us": round(mean["dense_decode_attn"], 2),
         "speedup_vs_dense": round(mean["dense_decode_attn"] / mean["sparse_decode_attn"], 3),
         "e2e_speedup_vs_dense": round(mean["dense_decode_attn"] / (mean["topk_index"] + mean["sparse_decode_attn"]), 3),
+        "step_us": round(mean["sparse_decode_step"], 2),
+        "step_speedup_vs_dense": round(mean["dense_decode_attn"] / mean["sparse_decode_step"], 3),
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
         "algorithmic_bytes": {"topk_index": ab["topk"], "sparse_decode_attn": ab["sparse"],
-                              "dense_decode_attn": ab["dense"]},
+                              "dense_decode_attn": ab["dense"], "sparse_decode_step": ab["step"]},
         "distinct_rows": ab["distinct_rows"],
         "selected_rows": ab["selected_rows"],
         "roofline": roofline("sparse_decode_attn", ab["sparse"]),
         "roofline_kernels": {
             "topk_index": roofline("topk_index", ab["topk"]),
             "dense_decode_attn": roofline("dense_decode_attn", ab["dense"]),
+            "sparse_decode_step": roofline("sparse_decode_step", ab["step"]),
         },
     }
     if args.cpu_seconds > 0:

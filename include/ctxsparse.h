@@ -127,6 +127,25 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
                              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * sparse_decode_step — the oracle-indexed decode step in one call: topk_index followed by
+ * sparse_decode_attn over the lists it selects (the end-to-end step whose indexer overhead the
+ * technical summary, section 3.C, counts against the sparse kernel's gain).  Same arguments and
+ * results as those two calls; `indices` (device int32 [B, T, Hq, k_max]) may be NULL when the
+ * lists themselves are not wanted.  For k_max <= max_len / 16 each row's selection and its
+ * attention run in one workgroup on the scores the indexer already computed, so only the V rows
+ * of the selected positions are read for the attention; otherwise the two calls run back to back
+ * on `stream`.  out / lse agree with sparse_decode_attn over the exact top-k lists within the
+ * same tolerances (the scores come from the indexer's float32 dot products).
+ * Errors: as topk_index and sparse_decode_attn.
+ * ------------------------------------------------------------------------------------------ */
+size_t sparse_decode_step_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                         int32_t k_max);
+cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             float sm_scale, const int32_t* k_per_req, int32_t k_max,
+                             int32_t* indices, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * dense_decode_attn — the same-GPU dense baseline (a5): sparse_decode_attn with every visible
  * position selected, computed by streaming each (b, KV head)'s cache once for all G * T rows.
  * num_splits: pieces the sequence axis is cut into (0: automatic).

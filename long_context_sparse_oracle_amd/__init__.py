@@ -6,6 +6,8 @@ include/ctxsparse.h); this package is a thin ctypes binding with the same entry-
     topk_index(q, cache, k)                 -> int32 [B, T, Hq, k] selected positions
     sparse_decode_attn(q, cache, indices)   -> (out fp32 [B, T, Hq, d], lse fp32 [B, T, Hq])
     dense_decode_attn(q, cache)             -> (out, lse) over every visible position
+    sparse_decode_step(q, cache, k)         -> (out, lse): the indexer and the sparse attention
+                                               in one call (fused per row for k <= N/16)
     KVCache(k, v, seq_lens, page_table=...) -> contiguous or paged bf16 cache description
 
 Build the library with `python -m long_context_sparse_oracle_amd.build`.  Accessing any of the
@@ -21,6 +23,8 @@ _BINDING_NAMES = (
     "sparse_decode_attn_workspace_size",
     "dense_decode_attn",
     "dense_decode_attn_workspace_size",
+    "sparse_decode_step",
+    "sparse_decode_step_workspace_size",
     "LIB",
     "LIB_PATH",
 )

@@ -36,6 +36,8 @@ EXPORTS = (
     "sparse_decode_attn",
     "dense_decode_attn_workspace_size",
     "dense_decode_attn",
+    "sparse_decode_step_workspace_size",
+    "sparse_decode_step",
 )
 
 
@@ -91,6 +93,10 @@ def _load() -> ctypes.CDLL:
     lib.dense_decode_attn_workspace_size.restype = sz
     lib.dense_decode_attn.argtypes = [shp, P, kvp, f32, i32, P, P, P, sz, P]
     lib.dense_decode_attn.restype = ctypes.c_int
+    lib.sparse_decode_step_workspace_size.argtypes = [shp, kvp, i32]
+    lib.sparse_decode_step_workspace_size.restype = sz
+    lib.sparse_decode_step.argtypes = [shp, P, kvp, f32, P, i32, P, P, P, P, sz, P]
+    lib.sparse_decode_step.restype = ctypes.c_int
     return lib
 
 
@@ -195,6 +201,21 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[int, in
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
+def _k_arg(k, k_max, shp, device):
+    """(k tensor kept alive, device pointer or 0, k_max) from an int or an int32 tensor [B]."""
+    if isinstance(k, torch.Tensor):
+        if k.dtype != torch.int32 or not k.is_contiguous():
+            raise TypeError("k per request must be a contiguous int32 tensor")
+        if k_max is None:
+            raise ValueError("k_max is required with a per-request k tensor")
+        return k, k.data_ptr(), int(k_max)
+    k_max = int(k) if k_max is None else int(k_max)
+    if int(k) == k_max:
+        return k, 0, k_max
+    kt = torch.full((shp.batch,), int(k), dtype=torch.int32, device=device)
+    return kt, kt.data_ptr(), k_max
+
+
 def topk_index_workspace_size(q: torch.Tensor, cache: KVCache, k_max: int) -> int:
     shp = _shape(q, cache)
     desc = cache.desc()
@@ -214,18 +235,7 @@ def topk_index(
     """Oracle top-k indexer: int32 [B, T, Hq, k_max] of selected positions per row (ascending,
     -1 padded).  `k` is one int for every request or an int32 device tensor [B]."""
     shp = _shape(q, cache)
-    if isinstance(k, torch.Tensor):
-        if k.dtype != torch.int32 or not k.is_contiguous():
-            raise TypeError("k per request must be a contiguous int32 tensor")
-        if k_max is None:
-            raise ValueError("k_max is required with a per-request k tensor")
-        kptr = k.data_ptr()
-    else:
-        k_max = int(k) if k_max is None else int(k_max)
-        kptr = 0 if int(k) == k_max else None
-        if kptr is None:
-            k = torch.full((shp.batch,), int(k), dtype=torch.int32, device=q.device)
-            kptr = k.data_ptr()
+    k, kptr, k_max = _k_arg(k, k_max, shp, q.device)
     if indices is None:
         indices = torch.empty((shp.batch, shp.q_len, shp.num_q_heads, k_max), dtype=torch.int32,
                               device=q.device)
@@ -311,4 +321,45 @@ def dense_decode_attn(
                                _scale(shp.head_dim, sm_scale), int(num_splits), out.data_ptr(),
                                lse.data_ptr(), wptr, wbytes, _stream(q))
     _check("dense_decode_attn", st)
+    return out, lse
+
+
+def sparse_decode_step_workspace_size(q: torch.Tensor, cache: KVCache, k_max: int) -> int:
+    shp = _shape(q, cache)
+    desc = cache.desc()
+    return int(LIB.sparse_decode_step_workspace_size(ctypes.byref(shp), ctypes.byref(desc), int(k_max)))
+
+
+def sparse_decode_step(
+    q: torch.Tensor,
+    cache: KVCache,
+    k: Union[int, torch.Tensor],
+    *,
+    k_max: Optional[int] = None,
+    sm_scale: Optional[float] = None,
+    indices: Optional[torch.Tensor] = None,
+    return_indices: bool = False,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+):
+    """The oracle-indexed decode step in one call (topk_index, then sparse_decode_attn over its
+    lists): returns (out, lse), or (out, lse, indices) with return_indices or an `indices`
+    tensor given."""
+    shp = _shape(q, cache)
+    k, kptr, k_max = _k_arg(k, k_max, shp, q.device)
+    if indices is None and return_indices:
+        indices = torch.empty((shp.batch, shp.q_len, shp.num_q_heads, k_max), dtype=torch.int32,
+                              device=q.device)
+    out, lse = _outputs(shp, q.device, out, lse)
+    desc = cache.desc()
+    need = int(LIB.sparse_decode_step_workspace_size(ctypes.byref(shp), ctypes.byref(desc), k_max))
+    wptr, wbytes = _workspace(need, q.device, workspace)
+    st = LIB.sparse_decode_step(ctypes.byref(shp), q.data_ptr(), ctypes.byref(desc),
+                                _scale(shp.head_dim, sm_scale), kptr, k_max,
+                                indices.data_ptr() if indices is not None else 0, out.data_ptr(),
+                                lse.data_ptr(), wptr, wbytes, _stream(q))
+    _check("sparse_decode_step", st)
+    if indices is not None:
+        return out, lse, indices
     return out, lse

@@ -248,27 +248,15 @@ const char* cs_status_str(cs_status s) {
 
 int32_t cs_version(void) { return 100; }
 
-size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max) {
-  (void)k_max;
-  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK) return 0;
-  return topk_ws(shape, kv);
-}
-
-cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
-                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  cs_status st = check_shape(shape);
-  if (st != CS_OK) return st;
-  if ((st = check_kv(shape, kv)) != CS_OK) return st;
-  if (!q || !indices || !aligned(q, 16) || !aligned(indices, 4)) return CS_ERR_INVALID_ARG;
-  if (k_per_req && !aligned(k_per_req, 4)) return CS_ERR_INVALID_ARG;
-  if (k_max < 1 || k_max > kv->max_len) return CS_ERR_INVALID_ARG;
-  if (!std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
-  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
-  const size_t need = topk_ws(shape, kv);
-  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
-
+cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                           float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
+                           void* workspace) {
   cs::TopkLaunch a;
+  a.fused = false;
+  a.sel_pos = nullptr;
+  a.sel_score = nullptr;
+  a.out = nullptr;
+  a.lse = nullptr;
   a.q = static_cast<const uint16_t*>(q);
   a.kv = make_kv(shape, kv);
   a.B = shape->batch;
@@ -293,8 +281,62 @@ cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_de
   a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.indices = indices;
+  return a;
+}
+
+size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max) {
+  (void)k_max;
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK) return 0;
+  return topk_ws(shape, kv);
+}
+
+cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !indices || !aligned(q, 16) || !aligned(indices, 4)) return CS_ERR_INVALID_ARG;
+  if (k_per_req && !aligned(k_per_req, 4)) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len) return CS_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
+  const size_t need = topk_ws(shape, kv);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
+
+  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, workspace);
   hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+cs::AttnLaunch sparse_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             const int32_t* indices, int32_t k_max, float sm_scale,
+                             const SparsePlan& plan, float* out, float* lse, void* workspace) {
+  const int S = plan.S;
+  cs::AttnLaunch a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = make_kv(shape, kv);
+  a.B = shape->batch;
+  a.T = shape->q_len;
+  a.Hq = shape->num_q_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.GT = gt_of(shape);
+  a.D = shape->head_dim;
+  a.rows = (int)rows_of(shape);
+  a.paged = kv->layout == CS_KV_PAGED;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.indices = indices;
+  a.k_max = k_max;
+  a.S = S;
+  a.chunk = plan.chunk;
+  a.waves = plan.waves;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
+                    : nullptr;
+  a.out = out;
+  a.lse = lse;
+  return a;
 }
 
 size_t sparse_decode_attn_workspace_size(const cs_decode_shape* shape, int32_t k_max,
@@ -319,30 +361,72 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   const size_t need = attn_ws(shape, S);
   if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
 
-  cs::AttnLaunch a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.kv = make_kv(shape, kv);
-  a.B = shape->batch;
-  a.T = shape->q_len;
-  a.Hq = shape->num_q_heads;
-  a.G = shape->num_q_heads / shape->num_kv_heads;
-  a.GT = gt_of(shape);
-  a.D = shape->head_dim;
-  a.rows = (int)rows_of(shape);
-  a.paged = kv->layout == CS_KV_PAGED;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.indices = indices;
-  a.k_max = k_max;
-  a.S = S;
-  a.chunk = plan.chunk;
-  a.waves = plan.waves;
-  char* ws = static_cast<char*>(workspace);
-  a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
-                    : nullptr;
-  a.out = out;
-  a.lse = lse;
+  cs::AttnLaunch a = sparse_launch(shape, q, kv, indices, k_max, sm_scale, plan, out, lse, workspace);
   hipError_t e = cs::launch_sparse(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+// ---- fused decode step: indexer + sparse attention in one call
+// Workspace: the indexer's, then the selected lists (int32 positions and float32 scores,
+// [rows, k_max] each), then the sparse attention's partials on the full-score path.
+struct StepWs {
+  size_t topk, sel_pos, sel_score, attn, total;
+};
+
+StepWs step_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max) {
+  const size_t rows = (size_t)rows_of(s);
+  StepWs w;
+  w.topk = 0;
+  w.sel_pos = align_up(topk_ws(s, kv));
+  w.sel_score = w.sel_pos + align_up(rows * (size_t)k_max * sizeof(int32_t));
+  w.attn = w.sel_score + align_up(rows * (size_t)k_max * sizeof(float));
+  w.total = w.attn + attn_ws(s, sparse_plan(s, k_max, 0).S);
+  return w;
+}
+
+size_t sparse_decode_step_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                         int32_t k_max) {
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK || k_max < 1 || k_max > kv->max_len)
+    return 0;
+  return step_ws_layout(shape, kv, k_max).total;
+}
+
+cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             float sm_scale, const int32_t* k_per_req, int32_t k_max,
+                             int32_t* indices, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !out || !lse || !aligned(q, 16) || !aligned(out, 4) || !aligned(lse, 4))
+    return CS_ERR_INVALID_ARG;
+  if ((indices && !aligned(indices, 4)) || (k_per_req && !aligned(k_per_req, 4))) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
+  const StepWs lay = step_ws_layout(shape, kv, k_max);
+  if ((st = check_ws(workspace, workspace_bytes, lay.total)) != CS_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* sel_pos = reinterpret_cast<int32_t*>(ws + lay.sel_pos);
+  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws + lay.topk);
+  if (a.filtered) {
+    // selection and attention of a row in one workgroup, on the candidates' own scores
+    a.fused = true;
+    a.sel_pos = sel_pos;
+    a.sel_score = reinterpret_cast<float*>(ws + lay.sel_score);
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = cs::launch_topk(a, hs);
+    return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+  }
+  // full-score path: the index lists (the caller's buffer, else the workspace), then attention
+  int32_t* idx = indices ? indices : sel_pos;
+  a.indices = idx;
+  hipError_t e = cs::launch_topk(a, hs);
+  if (e != hipSuccess) return CS_ERR_HIP;
+  const SparsePlan plan = sparse_plan(shape, k_max, 0);
+  cs::AttnLaunch b = sparse_launch(shape, q, kv, idx, k_max, sm_scale, plan, out, lse, ws + lay.attn);
+  e = cs::launch_sparse(b, hs);
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
 }
 

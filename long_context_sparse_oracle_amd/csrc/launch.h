@@ -29,6 +29,12 @@ struct TopkLaunch {
   bool filtered;
   uint32_t* sample_keys;  // [rows, 1024]: ordered keys of the sampled scores
   uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
+  // fused decode step (filtered path): selection and attention per row in one kernel
+  bool fused;
+  int32_t* sel_pos;   // [rows, k_max]
+  float* sel_score;   // [rows, k_max]
+  float* out;         // [rows, D]
+  float* lse;         // [rows]
   int cand_chunk, cand_chunks;
 };
 

@@ -939,13 +939,21 @@ __device__ uint32_t radix_kth(KeyAt key_at, int total, int kk, uint32_t kmin, ui
   return prefix;
 }
 
+// Where a selection goes: the index row (or nullptr) and, for the fused decode step, the row's
+// selected (position, score) list (or nullptrs).
+struct SelOut {
+  int32_t* idx;
+  int32_t* pos;
+  float* score;
+};
+
 // Emission of one block of list items in list order: item fb + e (e < kCsPer) of this thread, key
 // keys[e], position pos[e]; selected are keys > kstar and the first `need` keys == kstar (unless
 // take_all_eq).  eq_base / out_base carry the counts of the earlier blocks.
 __device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&keys)[kCsPer],
                                            const uint32_t (&pos)[kCsPer], uint32_t kstar, uint32_t need,
                                            bool take_all_eq, uint32_t& eq_base, uint32_t& out_base,
-                                           int32_t* __restrict__ out, SelShared& sh) {
+                                           const SelOut& so, SelShared& sh) {
   uint32_t eqc = 0;
 #pragma unroll
   for (int e = 0; e < kCsPer; ++e) eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
@@ -965,8 +973,16 @@ __device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&k
   }
   uint32_t o = out_base + block_excl_scan<kCsWaves>(selc, sh.wsum, &sel_tot);
 #pragma unroll
-  for (int e = 0; e < kCsPer; ++e)
-    if ((selm >> e) & 1u) out[o++] = (int32_t)pos[e];
+  for (int e = 0; e < kCsPer; ++e) {
+    if ((selm >> e) & 1u) {
+      if (so.idx) so.idx[o] = (int32_t)pos[e];
+      if (so.pos) {
+        so.pos[o] = (int32_t)pos[e];
+        so.score[o] = key_to_float(keys[e]);
+      }
+      ++o;
+    }
+  }
   eq_base += eq_tot;
   out_base += sel_tot;
 }
@@ -974,7 +990,7 @@ __device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&k
 // Writes, in list order, the kk items of the largest keys (ties at the k-th key: earliest items)
 // and pads out to k_max with -1.  Keys and positions come from src (list in global memory).
 template <class Src>
-__device__ void select_ordered(const Src& src, int total, int kk, int k_max, int32_t* __restrict__ out,
+__device__ void select_ordered(const Src& src, int total, int kk, int k_max, const SelOut& so,
                                uint32_t* hist, SelShared& sh) {
   const int tid = threadIdx.x;
   uint32_t need, cnt_eq;
@@ -988,17 +1004,184 @@ __device__ void select_ordered(const Src& src, int total, int kk, int k_max, int
 #pragma unroll
     for (int e = 0; e < kCsPer; ++e) keys[e] = fb + e < total ? src.key(fb + e) : 0u;
     src.pos8(fb, total, 0xffu, pos);
-    emit_block(fb, total, keys, pos, kstar, need, take_all_eq, eq_base, out_base, out, sh);
+    emit_block(fb, total, keys, pos, kstar, need, take_all_eq, eq_base, out_base, so, sh);
   }
-  for (int i = kk + tid; i < k_max; i += kCsThreads) out[i] = -1;
+  if (so.idx)
+    for (int i = kk + tid; i < k_max; i += kCsThreads) so.idx[i] = -1;
 }
 
+// Attention of one row over its selected list (positions and scaled scores, kk entries), for the
+// fused decode step: the scores come with the list, so only V rows are read.  Each of the
+// kCsWaves waves takes kCsAttnEntries entries per round (D/8 lanes per position, all V loads of
+// the round in flight before use), keeps an online softmax in log2 units, and the position groups
+// and waves are merged at the end (lane shuffles, then `red`: kCsWaves * (D + 2) floats of LDS).
+constexpr int kCsAttnEntries = 64;
 template <int D, bool PAGED>
+__device__ void attend_list(const KVArgs& kv, int b, int h, const int32_t* __restrict__ pos,
+                            const float* __restrict__ score, int kk, float* red,
+                            float* __restrict__ out_row, float* __restrict__ lse_row) {
+  constexpr int LPP = D / 8, PPW = kWave / LPP, NSTEP = kCsAttnEntries / PPW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = lane / LPP, c = lane - (lane / LPP) * LPP;
+  float m = -INFINITY, l = 0.f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int base = wave * kCsAttnEntries; base < kk; base += kCsWaves * kCsAttnEntries) {
+    const bool mine_ok = base + lane < kk;
+    const int my_pos = mine_ok ? pos[base + lane] : 0;
+    const float my_s = mine_ok ? score[base + lane] * kLog2e : -INFINITY;
+    int idx[NSTEP];
+    float sv[NSTEP];
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) {
+      idx[u] = __shfl(my_pos, u * PPW + p);
+      sv[u] = __shfl(my_s, u * PPW + p);
+    }
+    uint4 vr[NSTEP];
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) vr[u] = ld16(kv.v + kv_row<D, PAGED>(kv, b, h, idx[u]) + c * 8);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) mx = fmaxf(mx, sv[u]);
+    const float m_new = fmaxf(m, mx);
+    if (m_new != -INFINITY) {
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < NSTEP; ++u) {
+        const float w = fast_exp2(sv[u] - m_new);
+        l += w;
+        float vf[8];
+        unpack8(vr[u], vf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(w, vf[i], o[i]);
+      }
+      m = m_new;
+    }
+  }
+#pragma unroll
+  for (int x = LPP; x < kWave; x *= 2) {
+    const float m_o = __shfl_xor(m, x);
+    const float l_o = __shfl_xor(l, x);
+    const float M = fmaxf(m, m_o);
+    const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float bw = m_o == -INFINITY ? 0.f : fast_exp2(m_o - M);
+    l = a * l + bw * l_o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = a * o[i] + bw * __shfl_xor(o[i], x);
+    m = M;
+  }
+  float* red_m = red;
+  float* red_l = red + kCsWaves;
+  float* red_o = red + 2 * kCsWaves;  // [kCsWaves][D]
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_l[wave] = l;
+  }
+  if (p == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red_o[wave * D + c * 8 + i] = o[i];
+  }
+  __syncthreads();
+  for (int col = tid; col < D; col += kCsThreads) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kCsWaves; ++w) M = fmaxf(M, red_m[w]);
+    float Lsum = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kCsWaves; ++w) {
+        const float wt = fast_exp2(red_m[w] - M);
+        Lsum = fmaf(wt, red_l[w], Lsum);
+        O = fmaf(wt, red_o[w * D + col], O);
+      }
+    }
+    out_row[col] = Lsum > 0.f ? O / Lsum : 0.f;
+    if (col == 0) *lse_row = Lsum > 0.f ? (M + fast_log2(Lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+// The candidate part of cand_select_kernel: select from the row's slots.
+__device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, int kk, int k_max,
+                          int row, float* __restrict__ region, int64_t score_stride, int chunks,
+                          const uint32_t* prefix_s, uint32_t* lds_key, int lds_cap, uint32_t* hist,
+                          SelShared& sh) {
+  const int tid = threadIdx.x;
+  CandSource src;
+  src.base = reinterpret_cast<const uint2*>(region + (int64_t)row * score_stride);
+  src.prefix = prefix_s;
+  src.nsub = nsub;
+  src.cap = cap;
+  src.nsub_all = chunks * kCandWaves;
+  src.lds_key = nullptr;
+  if (total > (uint32_t)lds_cap) {  // too many to hold: every pass reads the slots
+    select_ordered(src, (int)total, kk, k_max, so, hist, sh);
+    return;
+  }
+  // keys into LDS and positions into registers, kCsPer consecutive items per thread and block
+  // (the same items the emission gives this thread), loads of a block in flight together
+  if (tid == 0) {
+    sh.kmin = 0xffffffffu;
+    sh.kmax = 0u;
+  }
+  __syncthreads();
+  uint32_t preg[kCsMaxBlocks][kCsPer];
+  uint32_t lmin = 0xffffffffu, lmax = 0u;
+#pragma unroll
+  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
+    if (blk * kCsThreads * kCsPer >= (int)total) break;
+    int64_t off[kCsPer];
+    src.offsets(fb, (int)total, off);
+    uint2 pr[kCsPer];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) pr[e] = src.base[off[e]];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) {
+      preg[blk][e] = pr[e].x;
+      if (fb + e < (int)total) {
+        const uint32_t key = ord_key(__uint_as_float(pr[e].y));
+        lds_key[fb + e] = key;
+        lmin = min(lmin, key);
+        lmax = max(lmax, key);
+      }
+    }
+  }
+  atomicMin(&sh.kmin, lmin);
+  atomicMax(&sh.kmax, lmax);
+  __syncthreads();
+  uint32_t need, cnt_eq;
+  const uint32_t kstar = radix_kth([&](int f) { return lds_key[f]; }, (int)total, kk, sh.kmin, sh.kmax,
+                                   hist, sh, need, cnt_eq);
+  const bool take_all_eq = cnt_eq == need;
+  uint32_t eq_base = 0, out_base = 0;
+#pragma unroll
+  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+    if (blk * kCsThreads * kCsPer >= (int)total) break;
+    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
+    uint32_t keys[kCsPer];
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) keys[e] = fb + e < (int)total ? lds_key[fb + e] : 0u;
+    emit_block(fb, (int)total, keys, preg[blk], kstar, need, take_all_eq, eq_base, out_base, so, sh);
+  }
+  if (so.idx)
+    for (int i = kk + tid; i < k_max; i += kCsThreads) so.idx[i] = -1;
+}
+
+
+// FUSED (the decode step): the selection also goes to the row's (position, score) list in
+// sel_pos / sel_score, the workgroup then attends to it (attend_list) and writes out / lse;
+// indices may then be nullptr.
+template <int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
     const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
     const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int lds_cap,
-    int32_t* __restrict__ indices) {
+    int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
+    float* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
   __shared__ SelShared sh;
   __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
@@ -1013,10 +1196,20 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
   int kb = k_per_req ? k_per_req[b] : k_max;
   kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
   const int kk = min(kb, vis);
-  int32_t* out = indices + (int64_t)row * k_max;
+  SelOut so;
+  so.idx = indices ? indices + (int64_t)row * k_max : nullptr;
+  so.pos = FUSED ? sel_pos + (int64_t)row * k_max : nullptr;
+  so.score = FUSED ? sel_score + (int64_t)row * k_max : nullptr;
   const int tid = threadIdx.x;
-  if (kk == vis || kk == 0) {  // everything visible is selected, or nothing
-    for (int i = tid; i < k_max; i += kCsThreads) out[i] = i < kk ? i : -1;
+  // nothing to select; or (index-only) everything visible is selected -- the fused step needs the
+  // scores of every visible position then, which its fallback computes
+  if (kk == 0 || (!FUSED && kk == vis)) {
+    if (so.idx)
+      for (int i = tid; i < k_max; i += kCsThreads) so.idx[i] = i < kk ? i : -1;
+    if (FUSED) {
+      for (int i = tid; i < D; i += kCsThreads) out[(int64_t)row * D + i] = 0.f;
+      if (tid == 0) lse[row] = -INFINITY;
+    }
     return;
   }
 
@@ -1066,68 +1259,16 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
       if (ok && cdim == 0) srow[n] = dot * scale;
     }
     __syncthreads();
-    select_ordered(DenseSource{srow}, vis, kk, k_max, out, hist, sh);
-    return;
+    select_ordered(DenseSource{srow}, vis, kk, k_max, so, hist, sh);
+  } else {
+    cand_path(total, nsub, cap, so, kk, k_max, row, region, score_stride, chunks, prefix_s, lds_key,
+              lds_cap, hist, sh);
   }
-
-  CandSource src;
-  src.base = reinterpret_cast<const uint2*>(region + (int64_t)row * score_stride);
-  src.prefix = prefix_s;
-  src.nsub = nsub;
-  src.cap = cap;
-  src.nsub_all = chunks * kCandWaves;
-  src.lds_key = nullptr;
-  if (total > (uint32_t)lds_cap) {  // too many to hold: every pass reads the slots
-    select_ordered(src, (int)total, kk, k_max, out, hist, sh);
-    return;
+  if constexpr (FUSED) {
+    __syncthreads();  // the selected list is complete, LDS free again
+    attend_list<D, PAGED>(kv, b, hq / G, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
+                          out + (int64_t)row * D, lse + row);
   }
-  // keys into LDS and positions into registers, kCsPer consecutive items per thread and block
-  // (the same items the emission gives this thread), loads of a block in flight together
-  if (tid == 0) {
-    sh.kmin = 0xffffffffu;
-    sh.kmax = 0u;
-  }
-  __syncthreads();
-  uint32_t preg[kCsMaxBlocks][kCsPer];
-  uint32_t lmin = 0xffffffffu, lmax = 0u;
-#pragma unroll
-  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
-    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
-    if (blk * kCsThreads * kCsPer >= (int)total) break;
-    int64_t off[kCsPer];
-    src.offsets(fb, (int)total, off);
-    uint2 pr[kCsPer];
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e) pr[e] = src.base[off[e]];
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e) {
-      preg[blk][e] = pr[e].x;
-      if (fb + e < (int)total) {
-        const uint32_t key = ord_key(__uint_as_float(pr[e].y));
-        lds_key[fb + e] = key;
-        lmin = min(lmin, key);
-        lmax = max(lmax, key);
-      }
-    }
-  }
-  atomicMin(&sh.kmin, lmin);
-  atomicMax(&sh.kmax, lmax);
-  __syncthreads();
-  uint32_t need, cnt_eq;
-  const uint32_t kstar = radix_kth([&](int f) { return lds_key[f]; }, (int)total, kk, sh.kmin, sh.kmax,
-                                   hist, sh, need, cnt_eq);
-  const bool take_all_eq = cnt_eq == need;
-  uint32_t eq_base = 0, out_base = 0;
-#pragma unroll
-  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
-    if (blk * kCsThreads * kCsPer >= (int)total) break;
-    const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
-    uint32_t keys[kCsPer];
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e) keys[e] = fb + e < (int)total ? lds_key[fb + e] : 0u;
-    emit_block(fb, (int)total, keys, preg[blk], kstar, need, take_all_eq, eq_base, out_base, out, sh);
-  }
-  for (int i = kk + tid; i < k_max; i += kCsThreads) out[i] = -1;
 }
 
 // ============================================================================ launchers
@@ -1187,14 +1328,14 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   int lds_cap = (int)(((int64_t)a.k_max * 9 / 2 + 255) / 256 * 256);
   if (lds_cap > kCsMaxBlocks * kCsThreads * kCsPer) lds_cap = kCsMaxBlocks * kCsThreads * kCsPer;
   const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
-  auto sel = cand_select_kernel<D, PAGED>;
+  auto sel = a.fused ? cand_select_kernel<D, PAGED, true> : cand_select_kernel<D, PAGED, false>;
   if (lds > 65536) {
     e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
                      a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                     a.cand_chunks, a.k_max, lds_cap, a.indices);
+                     a.cand_chunks, a.k_max, lds_cap, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("topk_index", "sparse_decode_attn", "dense_decode_attn", "topk_index_workspace_size",
               "sparse_decode_attn_workspace_size", "dense_decode_attn_workspace_size",
-              "cs_status_str", "cs_version"):
+              "sparse_decode_step", "sparse_decode_step_workspace_size", "cs_status_str", "cs_version"):
         assert n in names
 
 
@@ -175,6 +175,30 @@ def test_attention_arguments(lib):
     need = L.dense_decode_attn_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 4)
     assert need > 0
     assert _dense(L, _shape(), _kv(), splits=4, ws_bytes=need - 1) == WS_SMALL
+
+
+def _step(L, shape, kv, k_max=10, scale=0.088, ws=FAKE, ws_bytes=1 << 40, q=FAKE, idx=None, out=FAKE,
+          lse=FAKE):
+    return L.sparse_decode_step(ctypes.byref(shape), q, ctypes.byref(kv), scale, None, k_max, idx, out,
+                                lse, ws, ws_bytes, None)
+
+
+def test_step_arguments(lib):
+    L = lib.LIB
+    assert _step(L, _shape(d=96), _kv()) == UNSUPPORTED
+    assert _step(L, _shape(), _kv(k=0)) == INVALID
+    assert _step(L, _shape(), _kv(), k_max=0) == INVALID
+    assert _step(L, _shape(), _kv(max_len=50), k_max=51) == INVALID
+    assert _step(L, _shape(), _kv(), scale=float("nan")) == INVALID
+    assert _step(L, _shape(), _kv(), q=FAKE + 4) == INVALID
+    assert _step(L, _shape(), _kv(), out=0) == INVALID
+    assert _step(L, _shape(), _kv(), lse=0) == INVALID
+    assert _step(L, _shape(), _kv(), idx=FAKE + 2) == INVALID
+    assert _step(L, _shape(), _kv(max_len=262145), k_max=10) == UNSUPPORTED
+    need = L.sparse_decode_step_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10)
+    assert need >= L.topk_index_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10)
+    assert _step(L, _shape(), _kv(), ws_bytes=need - 1) == WS_SMALL
+    assert L.sparse_decode_step_workspace_size(ctypes.byref(_shape(d=96)), ctypes.byref(_kv()), 10) == 0
 
 
 def test_workspace_sizes(lib):
