@@ -346,7 +346,8 @@ def main():
 
     def roofline(name, bytes_per_launch):
         achieved = bytes_per_launch / (mean[name] * 1e-6) / 1e9
-        tr = traffic.get(args.workload, {}).get(name)
+        tag = args.workload + ("_" + args.sweep_k if args.sweep_k else "")
+        tr = traffic.get(tag, {}).get(name)
         tr_val = None
         if tr and tr.get("source_sha256") == source_hash(name):
             tr_val = tr.get("bytes_per_launch")

@@ -146,6 +146,65 @@ cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const 
                              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Reduced-byte indexer.  The technical summary (section 3.C, indexing-overhead bullet) counts
+ * an indexer's own cost against the sparse kernel's gain and estimates it with an indexer that
+ * scores a reduced form of each key.  This library's reduced form is an int8 key sketch: a key
+ * row K_n of d bf16 values is stored as d int8 codes and one float32 scale,
+ *   scale_n = max_i |K_n,i| / 127,   code_n,i = rint(K_n,i / scale_n)   (clamped to +-127),
+ * divisions correctly rounded in float32, rint rounding half to even, a zero row giving scale 0
+ * and codes 0.  The query row is quantised the same way, and the sketch score of position n is
+ *   a_n = (scale_q * scale_n) * (codes_q . codes_n)      (exact int32 dot product, two float32
+ *                                                         products rounded in that order),
+ * reading d + 4 bytes per position instead of 2 d.
+ *
+ * Selection of a row (k' = min(k_b, visible), m = cand_mult):
+ *   1. the min(m k', visible) visible positions with the largest a_n, the lower position first
+ *      among equal values (exact: count(a_n >= a sampled threshold) >= m k' is checked, and a
+ *      row short of candidates is rescored in full);
+ *   2. of those, the k' with the largest exact float32 scores s_n, as topk_index ranks them.
+ * With m k' >= visible the result is topk_index's.  Otherwise it may differ from the exact top-k
+ * where the sketch ranks an exact top-k position below m k' others.
+ * ------------------------------------------------------------------------------------------ */
+
+/* An int8 key sketch (host struct, device pointers owned by the caller). */
+typedef struct {
+  void* codes;   /* device int8 with the K cache's shape: [B, Hkv, max_len, d] (contiguous) or
+                    [num_pages, Hkv, page_size, d] (paged); 16-byte aligned */
+  float* scales; /* device float32 with the same shape without d */
+} cs_key_sketch;
+
+/* key_sketch_build — writes the sketch of key positions [max(0, L_b - last_n), L_b) of every
+ * request b and KV head (last_n = 0: every position [0, L_b)), through the page table for paged
+ * caches; other entries are left as they are.  A decode step that appended T tokens per request
+ * calls it with last_n = T.
+ * Errors: CS_ERR_INVALID_ARG for null or misaligned pointers and last_n < 0; as topk_index. */
+cs_status key_sketch_build(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t last_n,
+                           const cs_key_sketch* sketch, void* stream);
+
+/* topk_index_sketch — the reduced-byte indexer: topk_index's arguments and output layout, plus
+ * the sketch of the cache (current for every visible position) and cand_mult in [1, 64].
+ * Errors: as topk_index; CS_ERR_INVALID_ARG for a bad sketch or cand_mult; CS_ERR_UNSUPPORTED
+ * when one (request, KV head)'s candidate areas would span 2 GiB or more. */
+size_t topk_index_sketch_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                        int32_t k_max, int32_t cand_mult);
+cs_status topk_index_sketch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                            int32_t k_max, int32_t cand_mult, int32_t* indices, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* sparse_decode_step_sketch — sparse_decode_step with the reduced-byte indexer: each row's
+ * selection and its attention run in one workgroup, on the exact scores of the re-rank, so only
+ * the V rows of the selected positions are read for the attention.  `indices` may be NULL.
+ * Errors: as topk_index_sketch and sparse_decode_step. */
+size_t sparse_decode_step_sketch_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                                int32_t k_max, int32_t cand_mult);
+cs_status sparse_decode_step_sketch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                                    const cs_key_sketch* sketch, float sm_scale,
+                                    const int32_t* k_per_req, int32_t k_max, int32_t cand_mult,
+                                    int32_t* indices, float* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * dense_decode_attn — the same-GPU dense baseline (a5): sparse_decode_attn with every visible
  * position selected, computed by streaming each (b, KV head)'s cache once for all G * T rows.
  * num_splits: pieces the sequence axis is cut into (0: automatic).

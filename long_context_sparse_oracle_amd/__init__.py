@@ -8,6 +8,10 @@ include/ctxsparse.h); this package is a thin ctypes binding with the same entry-
     dense_decode_attn(q, cache)             -> (out, lse) over every visible position
     sparse_decode_step(q, cache, k)         -> (out, lse): the indexer and the sparse attention
                                                in one call (fused per row for k <= N/16)
+    key_sketch_build(cache)                 -> KeySketch: int8 codes + float32 scale per key row
+    topk_index_sketch(q, cache, sketch, k)  -> the reduced-byte indexer: cand_mult * k candidates
+                                               ranked on the sketch, re-ranked on exact scores
+    sparse_decode_step_sketch(q, cache, sketch, k) -> (out, lse) with that indexer, fused
     KVCache(k, v, seq_lens, page_table=...) -> contiguous or paged bf16 cache description
 
 Build the library with `python -m long_context_sparse_oracle_amd.build`.  Accessing any of the
@@ -25,6 +29,12 @@ _BINDING_NAMES = (
     "dense_decode_attn_workspace_size",
     "sparse_decode_step",
     "sparse_decode_step_workspace_size",
+    "KeySketch",
+    "key_sketch_build",
+    "topk_index_sketch",
+    "topk_index_sketch_workspace_size",
+    "sparse_decode_step_sketch",
+    "sparse_decode_step_sketch_workspace_size",
     "LIB",
     "LIB_PATH",
 )

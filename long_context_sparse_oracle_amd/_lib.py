@@ -38,6 +38,11 @@ EXPORTS = (
     "dense_decode_attn",
     "sparse_decode_step_workspace_size",
     "sparse_decode_step",
+    "key_sketch_build",
+    "topk_index_sketch_workspace_size",
+    "topk_index_sketch",
+    "sparse_decode_step_sketch_workspace_size",
+    "sparse_decode_step_sketch",
 )
 
 
@@ -63,6 +68,10 @@ class KVDesc(ctypes.Structure):
         ("page_table", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
     ]
+
+
+class KeySketchDesc(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -97,6 +106,17 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_step_workspace_size.restype = sz
     lib.sparse_decode_step.argtypes = [shp, P, kvp, f32, P, i32, P, P, P, P, sz, P]
     lib.sparse_decode_step.restype = ctypes.c_int
+    skp = ctypes.POINTER(KeySketchDesc)
+    lib.key_sketch_build.argtypes = [shp, kvp, i32, skp, P]
+    lib.key_sketch_build.restype = ctypes.c_int
+    lib.topk_index_sketch_workspace_size.argtypes = [shp, kvp, i32, i32]
+    lib.topk_index_sketch_workspace_size.restype = sz
+    lib.topk_index_sketch.argtypes = [shp, P, kvp, skp, f32, P, i32, i32, P, P, sz, P]
+    lib.topk_index_sketch.restype = ctypes.c_int
+    lib.sparse_decode_step_sketch_workspace_size.argtypes = [shp, kvp, i32, i32]
+    lib.sparse_decode_step_sketch_workspace_size.restype = sz
+    lib.sparse_decode_step_sketch.argtypes = [shp, P, kvp, skp, f32, P, i32, i32, P, P, P, P, sz, P]
+    lib.sparse_decode_step_sketch.restype = ctypes.c_int
     return lib
 
 
@@ -360,6 +380,133 @@ def sparse_decode_step(
                                 indices.data_ptr() if indices is not None else 0, out.data_ptr(),
                                 lse.data_ptr(), wptr, wbytes, _stream(q))
     _check("sparse_decode_step", st)
+    if indices is not None:
+        return out, lse, indices
+    return out, lse
+
+
+# ---------------------------------------------------------------------------- reduced-byte indexer
+class KeySketch:
+    """int8 sketch of a KVCache's keys: codes int8 with K's shape, scales float32 with K's shape
+    without the last axis (tensors owned by the caller).  Fill it with key_sketch_build."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        if codes.dtype != torch.int8 or not codes.is_contiguous() or codes.dim() != 4:
+            raise TypeError("codes must be a contiguous 4-d int8 tensor")
+        if scales.dtype != torch.float32 or not scales.is_contiguous() or tuple(scales.shape) != tuple(codes.shape[:3]):
+            raise TypeError("scales must be a contiguous float32 tensor of codes.shape[:3]")
+        self.codes, self.scales = codes, scales
+
+    @classmethod
+    def empty_for(cls, cache: KVCache) -> "KeySketch":
+        codes = torch.zeros(cache.k.shape, dtype=torch.int8, device=cache.k.device)
+        scales = torch.zeros(cache.k.shape[:3], dtype=torch.float32, device=cache.k.device)
+        return cls(codes, scales)
+
+    def check(self, cache: KVCache) -> None:
+        if tuple(self.codes.shape) != tuple(cache.k.shape):
+            raise ValueError("the sketch's shape differs from the cache's K")
+
+    def desc(self) -> KeySketchDesc:
+        return KeySketchDesc(self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def key_sketch_build(cache: KVCache, sketch: Optional[KeySketch] = None, *, last_n: int = 0) -> KeySketch:
+    """Sketch key positions [max(0, L_b - last_n), L_b) of every request and KV head (last_n = 0:
+    all of [0, L_b)) into `sketch` (allocated when None); returns the sketch."""
+    if sketch is None:
+        sketch = KeySketch.empty_for(cache)
+    sketch.check(cache)
+    B = int(cache.seq_lens.numel())
+    shp = DecodeShape(B, 1, cache.num_kv_heads, cache.num_kv_heads, cache.head_dim)
+    desc = cache.desc()
+    sd = sketch.desc()
+    st = LIB.key_sketch_build(ctypes.byref(shp), ctypes.byref(desc), int(last_n), ctypes.byref(sd),
+                              _stream(cache.k))
+    _check("key_sketch_build", st)
+    return sketch
+
+
+def topk_index_sketch_workspace_size(q: torch.Tensor, cache: KVCache, k_max: int, cand_mult: int = 2) -> int:
+    shp = _shape(q, cache)
+    desc = cache.desc()
+    return int(LIB.topk_index_sketch_workspace_size(ctypes.byref(shp), ctypes.byref(desc), int(k_max),
+                                                    int(cand_mult)))
+
+
+def topk_index_sketch(
+    q: torch.Tensor,
+    cache: KVCache,
+    sketch: KeySketch,
+    k: Union[int, torch.Tensor],
+    *,
+    k_max: Optional[int] = None,
+    cand_mult: int = 2,
+    sm_scale: Optional[float] = None,
+    indices: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Reduced-byte indexer: cand_mult * k candidates per row ranked on the int8 key sketch, the
+    k best of them on exact scores; int32 [B, T, Hq, k_max] as topk_index."""
+    shp = _shape(q, cache)
+    sketch.check(cache)
+    k, kptr, k_max = _k_arg(k, k_max, shp, q.device)
+    if indices is None:
+        indices = torch.empty((shp.batch, shp.q_len, shp.num_q_heads, k_max), dtype=torch.int32,
+                              device=q.device)
+    desc = cache.desc()
+    sd = sketch.desc()
+    need = int(LIB.topk_index_sketch_workspace_size(ctypes.byref(shp), ctypes.byref(desc), k_max,
+                                                    int(cand_mult)))
+    wptr, wbytes = _workspace(need, q.device, workspace)
+    st = LIB.topk_index_sketch(ctypes.byref(shp), q.data_ptr(), ctypes.byref(desc), ctypes.byref(sd),
+                               _scale(shp.head_dim, sm_scale), kptr, k_max, int(cand_mult),
+                               indices.data_ptr(), wptr, wbytes, _stream(q))
+    _check("topk_index_sketch", st)
+    return indices
+
+
+def sparse_decode_step_sketch_workspace_size(q: torch.Tensor, cache: KVCache, k_max: int,
+                                             cand_mult: int = 2) -> int:
+    shp = _shape(q, cache)
+    desc = cache.desc()
+    return int(LIB.sparse_decode_step_sketch_workspace_size(ctypes.byref(shp), ctypes.byref(desc),
+                                                            int(k_max), int(cand_mult)))
+
+
+def sparse_decode_step_sketch(
+    q: torch.Tensor,
+    cache: KVCache,
+    sketch: KeySketch,
+    k: Union[int, torch.Tensor],
+    *,
+    k_max: Optional[int] = None,
+    cand_mult: int = 2,
+    sm_scale: Optional[float] = None,
+    indices: Optional[torch.Tensor] = None,
+    return_indices: bool = False,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+):
+    """The decode step with the reduced-byte indexer: (out, lse), or (out, lse, indices)."""
+    shp = _shape(q, cache)
+    sketch.check(cache)
+    k, kptr, k_max = _k_arg(k, k_max, shp, q.device)
+    if indices is None and return_indices:
+        indices = torch.empty((shp.batch, shp.q_len, shp.num_q_heads, k_max), dtype=torch.int32,
+                              device=q.device)
+    out, lse = _outputs(shp, q.device, out, lse)
+    desc = cache.desc()
+    sd = sketch.desc()
+    need = int(LIB.sparse_decode_step_sketch_workspace_size(ctypes.byref(shp), ctypes.byref(desc), k_max,
+                                                            int(cand_mult)))
+    wptr, wbytes = _workspace(need, q.device, workspace)
+    st = LIB.sparse_decode_step_sketch(ctypes.byref(shp), q.data_ptr(), ctypes.byref(desc), ctypes.byref(sd),
+                                       _scale(shp.head_dim, sm_scale), kptr, k_max, int(cand_mult),
+                                       indices.data_ptr() if indices is not None else 0, out.data_ptr(),
+                                       lse.data_ptr(), wptr, wbytes, _stream(q))
+    _check("sparse_decode_step_sketch", st)
     if indices is not None:
         return out, lse, indices
     return out, lse

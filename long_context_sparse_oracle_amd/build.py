@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libctxsparse.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "topk.hip", "attention.hip", "sketch.hip"]
 ARCH = "gfx950"
 
 

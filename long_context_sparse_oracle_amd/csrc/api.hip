@@ -141,6 +141,56 @@ bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
   return (int64_t)k_max * 16 <= kv->max_len && span < (1LL << 31);
 }
 
+// ---- reduced-byte indexer sizing
+constexpr int kMaxCandMult = 64;
+
+// Entries of a row's candidate list: min(cand_mult * k_max, max_len), rounded up to 64.
+int64_t sketch_list_stride(const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
+  int64_t n = (int64_t)cand_mult * k_max;
+  if (n > kv->max_len) n = kv->max_len;
+  return ceil_div(n, 64) * 64;
+}
+
+// The sketch path always runs the candidate pipeline, whose buffer resource spans the score areas
+// of one (request, KV head)'s rows.
+bool sketch_supported(const cs_decode_shape* s, const cs_kv_desc* kv) {
+  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
+  return span < (1LL << 31);
+}
+
+cs_status check_sketch(const cs_key_sketch* sk) {
+  if (!sk || !sk->codes || !sk->scales) return CS_ERR_INVALID_ARG;
+  if (!aligned(sk->codes, 16) || !aligned(sk->scales, 4)) return CS_ERR_INVALID_ARG;
+  return CS_OK;
+}
+
+// Workspace of the sketch indexer (and, with `step`, of the fused step): candidate slots, sample
+// keys, slot counts, the query rows' codes and scales, the candidate lists (positions, scores),
+// then the selected lists of the step.
+struct SketchWs {
+  size_t scores, keys, counts, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
+};
+
+SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult,
+                          bool step) {
+  const size_t rows = (size_t)rows_of(s);
+  int cc, cn;
+  cand_chunking(s, kv, &cc, &cn);
+  const size_t ls = (size_t)sketch_list_stride(kv, k_max, cand_mult);
+  SketchWs w;
+  w.scores = 0;
+  w.keys = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
+  w.q_codes = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
+  w.list_pos = w.q_scales + align_up(rows * sizeof(float));
+  w.list_score = w.list_pos + align_up(rows * ls * sizeof(int32_t));
+  w.sel_pos = w.list_score + align_up(rows * ls * sizeof(float));
+  w.sel_score = w.sel_pos + (step ? align_up(rows * (size_t)k_max * sizeof(int32_t)) : 0);
+  w.total = w.sel_score + (step ? align_up(rows * (size_t)k_max * sizeof(float)) : 0);
+  return w;
+}
+
 struct TopkWs {
   size_t scores, hist, keys, counts, total;
 };
@@ -253,6 +303,12 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
                            void* workspace) {
   cs::TopkLaunch a;
   a.fused = false;
+  a.sketch = false;
+  a.sk = cs::SketchArgs{nullptr, nullptr, nullptr, nullptr};
+  a.cand_mult = 1;
+  a.list_pos = nullptr;
+  a.list_score = nullptr;
+  a.list_stride = 0;
   a.sel_pos = nullptr;
   a.sel_score = nullptr;
   a.out = nullptr;
@@ -427,6 +483,112 @@ cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const 
   const SparsePlan plan = sparse_plan(shape, k_max, 0);
   cs::AttnLaunch b = sparse_launch(shape, q, kv, idx, k_max, sm_scale, plan, out, lse, ws + lay.attn);
   e = cs::launch_sparse(b, hs);
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+// ---- reduced-byte indexer
+cs_status key_sketch_build(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t last_n,
+                           const cs_key_sketch* sketch, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if ((st = check_sketch(sketch)) != CS_OK) return st;
+  if (last_n < 0) return CS_ERR_INVALID_ARG;
+  hipError_t e = cs::launch_key_sketch(make_kv(shape, kv), shape->batch, shape->head_dim, last_n,
+                                       static_cast<int8_t*>(sketch->codes), sketch->scales,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+namespace {
+
+cs_status check_sketch_call(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                            int32_t k_max, int32_t cand_mult, const int32_t* indices) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if ((st = check_sketch(sketch)) != CS_OK) return st;
+  if (!q || !aligned(q, 16)) return CS_ERR_INVALID_ARG;
+  if ((indices && !aligned(indices, 4)) || (k_per_req && !aligned(k_per_req, 4))) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (cand_mult < 1 || cand_mult > kMaxCandMult) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen || !sketch_supported(shape, kv)) return CS_ERR_UNSUPPORTED;
+  return CS_OK;
+}
+
+cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                             int32_t k_max, int32_t cand_mult, int32_t* indices, char* ws,
+                             const SketchWs& lay) {
+  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws);
+  a.filtered = true;
+  a.sketch = true;
+  a.cand_mult = cand_mult;
+  a.sk.codes = static_cast<const int8_t*>(sketch->codes);
+  a.sk.scales = sketch->scales;
+  a.sk.q_codes = reinterpret_cast<int8_t*>(ws + lay.q_codes);
+  a.sk.q_scales = reinterpret_cast<float*>(ws + lay.q_scales);
+  a.scores = reinterpret_cast<float*>(ws + lay.scores);
+  a.hist = nullptr;
+  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
+  a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);
+  a.list_score = reinterpret_cast<float*>(ws + lay.list_score);
+  a.list_stride = (int)sketch_list_stride(kv, k_max, cand_mult);
+  return a;
+}
+
+}  // namespace
+
+size_t topk_index_sketch_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max,
+                                        int32_t cand_mult) {
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK || k_max < 1 || k_max > kv->max_len ||
+      cand_mult < 1 || cand_mult > kMaxCandMult)
+    return 0;
+  return sketch_ws_layout(shape, kv, k_max, cand_mult, false).total;
+}
+
+cs_status topk_index_sketch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                            int32_t k_max, int32_t cand_mult, int32_t* indices, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  cs_status st = check_sketch_call(shape, q, kv, sketch, sm_scale, k_per_req, k_max, cand_mult, indices);
+  if (st != CS_OK) return st;
+  if (!indices) return CS_ERR_INVALID_ARG;
+  const SketchWs lay = sketch_ws_layout(shape, kv, k_max, cand_mult, false);
+  if ((st = check_ws(workspace, workspace_bytes, lay.total)) != CS_OK) return st;
+  cs::TopkLaunch a = sketch_launch(shape, q, kv, sketch, sm_scale, k_per_req, k_max, cand_mult, indices,
+                                   static_cast<char*>(workspace), lay);
+  hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+size_t sparse_decode_step_sketch_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
+                                                int32_t k_max, int32_t cand_mult) {
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK || k_max < 1 || k_max > kv->max_len ||
+      cand_mult < 1 || cand_mult > kMaxCandMult)
+    return 0;
+  return sketch_ws_layout(shape, kv, k_max, cand_mult, true).total;
+}
+
+cs_status sparse_decode_step_sketch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                                    const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                                    int32_t k_max, int32_t cand_mult, int32_t* indices, float* out,
+                                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  cs_status st = check_sketch_call(shape, q, kv, sketch, sm_scale, k_per_req, k_max, cand_mult, indices);
+  if (st != CS_OK) return st;
+  if (!out || !lse || !aligned(out, 4) || !aligned(lse, 4)) return CS_ERR_INVALID_ARG;
+  const SketchWs lay = sketch_ws_layout(shape, kv, k_max, cand_mult, true);
+  if ((st = check_ws(workspace, workspace_bytes, lay.total)) != CS_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  cs::TopkLaunch a = sketch_launch(shape, q, kv, sketch, sm_scale, k_per_req, k_max, cand_mult, indices, ws, lay);
+  a.fused = true;
+  a.sel_pos = reinterpret_cast<int32_t*>(ws + lay.sel_pos);
+  a.sel_score = reinterpret_cast<float*>(ws + lay.sel_score);
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
 }
 

@@ -12,6 +12,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------- bf16 unpacking
 // A bf16 is the upper half of a binary32, so widening is a shift (low half of a 32-bit word) or
@@ -34,12 +35,13 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over aligned groups of N lanes (N = 8 or 16); every lane of the group gets the total.
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of the group gets the total.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "group size");
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
+  if constexpr (N >= 8) v += dpp<0x141>(v);
   if constexpr (N == 16) v += dpp<0x140>(v);
   return v;
 }

@@ -12,6 +12,16 @@ namespace cs {
 constexpr int kSparseWaveEntries = 16;
 constexpr int kSparseWaves = 8;
 
+// int8 key sketch of the reduced-byte indexer: per key row, int8 codes in the K cache's layout
+// (element offset e of K holds code e) and one float32 scale (index e / D); the query rows'
+// codes and scales live in the indexer's workspace.
+struct SketchArgs {
+  const int8_t* codes;
+  const float* scales;
+  int8_t* q_codes;   // [rows, D]
+  float* q_scales;   // [rows]
+};
+
 struct TopkLaunch {
   const uint16_t* q;
   KVArgs kv;
@@ -36,6 +46,14 @@ struct TopkLaunch {
   float* out;         // [rows, D]
   float* lse;         // [rows]
   int cand_chunk, cand_chunks;
+  // reduced-byte indexer: candidates ranked on the sketch, cand_mult * k of them re-ranked on
+  // exact scores through the list area (positions and scores, list_stride entries per row)
+  bool sketch;
+  SketchArgs sk;
+  int cand_mult;
+  int32_t* list_pos;
+  float* list_score;
+  int list_stride;
 };
 
 struct AttnLaunch {
@@ -58,6 +76,12 @@ size_t select_lds_bytes(int max_len);
 int score_threads(int GT);  // workgroup size of the score kernel for G*T query rows
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+// int8 sketch of key rows [max(0, L_b - last_n), L_b) of every (request, KV head) (last_n <= 0:
+// all of [0, L_b)), and of `rows` contiguous query rows
+hipError_t launch_key_sketch(const KVArgs& kv, int B, int D, int last_n, int8_t* codes, float* scales,
+                             hipStream_t stream);
+hipError_t launch_q_sketch(const uint16_t* q, int rows, int D, int8_t* codes, float* scales,
+                           hipStream_t stream);
 hipError_t launch_sparse(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_dense(const AttnLaunch& a, hipStream_t stream);
 

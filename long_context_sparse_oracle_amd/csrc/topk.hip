@@ -535,16 +535,46 @@ constexpr int kTauWaves = 4;
 constexpr int kTauTilesPerWave = kTauSamples / kTauParts / 16 / kTauWaves;  // 4
 static_assert(kTauTilesPerWave * 16 * kTauWaves * kTauParts == kTauSamples, "sample tiling");
 
+// 16 bytes of int8 codes
+__device__ __forceinline__ uint4 ld16i8(const int8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Scores of one 16-position tile for the 4 MFMA rows 4 * (lane / 16) + i of this lane, from the
+// operand steps a (query rows) and kt (key rows, this lane's position lane % 16):
+//   exact   bf16 dot products times `scale`;
+//   SK      sketch scores (qsc[i] * ksc) * (c_q . c_k), the integer dot product exact in int32.
+template <bool SK, int KS>
+__device__ __forceinline__ void tile_scores(const uint4 (&a)[KS], const uint4 (&kt)[KS], float scale,
+                                            const float (&qsc)[4], float ksc, float (&sc)[4]) {
+  if constexpr (SK) {
+    i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]), __builtin_bit_cast(i32x4, kt[j]),
+                                                  acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (qsc[i] * ksc) * (float)acc[i];
+  } else {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]), __builtin_bit_cast(bf16x8, kt[j]),
+                                                    acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = acc[i] * scale;
+  }
+}
+
 // Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
 __device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L + kTauSamples - 1) / kTauSamples : 1; }
 
 // Ordered key of a sampled score; 0 marks "not a sample of this row" (every finite score has a
 // larger key).
-template <int D, bool PAGED>
+// SK: the scores are sketch scores (int8 codes of q and K, one MFMA step per 64 channels).
+template <int D, bool PAGED, bool SK>
 __global__ __launch_bounds__(kTauWaves * kWave) void sample_keys_kernel(
-    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
     uint32_t* __restrict__ keys) {
-  constexpr int KS = D / 32;
+  constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   const int bh = blockIdx.x;
   const int mt = blockIdx.y;
   const int part = blockIdx.z;
@@ -561,31 +591,36 @@ __global__ __launch_bounds__(kTauWaves * kWave) void sample_keys_kernel(
   const int m = lane & 15;
   const int g4 = lane >> 4;
 
-  bf16x8 a[KS];
+  uint4 a[KS];
   {
     const int r = r0 + m;
     if (r < GT) {
       const int t = r / G, gi = r - (r / G) * G;
-      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+      for (int j = 0; j < KS; ++j)
+        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
     } else {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
     }
   }
   // sample j = part * 256 + 16 * (wave * kTauTilesPerWave + u) + m at position j * stride
   // (loads clamped to the last sample)
   const int j0 = part * (kTauSamples / kTauParts) + 16 * wave * kTauTilesPerWave;
   uint4 kt[kTauTilesPerWave][KS];
+  float ksc[kTauTilesPerWave];  // SK: the sampled rows' scales
   const int jlast = max(ns - 1, 0);
 #pragma unroll
   for (int u = 0; u < kTauTilesPerWave; ++u) {
     const int j = min(j0 + 16 * u + m, jlast);
+    ksc[u] = 0.f;
     if (L > 0) {
-      const int64_t off = kv_row<D, PAGED>(kv, b, h, j * stride) + g4 * 8;
+      const int64_t off = kv_row<D, PAGED>(kv, b, h, j * stride);
 #pragma unroll
-      for (int kq = 0; kq < KS; ++kq) kt[u][kq] = ld16(kv.k + off + kq * 32);
+      for (int kq = 0; kq < KS; ++kq)
+        kt[u][kq] = SK ? ld16i8(sk.codes + off + g4 * 16 + kq * 64) : ld16(kv.k + off + g4 * 8 + kq * 32);
+      if constexpr (SK) ksc[u] = sk.scales[off / D];
     } else {
 #pragma unroll
       for (int kq = 0; kq < KS; ++kq) kt[u][kq] = make_uint4(0, 0, 0, 0);
@@ -593,25 +628,26 @@ __global__ __launch_bounds__(kTauWaves * kWave) void sample_keys_kernel(
   }
   int vis_i[4];
   uint32_t* krow[4];
+  float qsc[4];  // SK: scales of this lane's output rows
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = 4 * g4 + i;
     const int r = r0 + rl;
     const int t = r / G, gi = r - (r / G) * G;
+    const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
     vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
-    krow[i] = keys + (rl < rows_here ? (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples : 0);
+    krow[i] = keys + (rl < rows_here ? qr * kTauSamples : 0);
+    qsc[i] = SK && rl < rows_here ? sk.q_scales[qr] : 0.f;
   }
 #pragma unroll
   for (int u = 0; u < kTauTilesPerWave; ++u) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kq = 0; kq < KS; ++kq)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kq], __builtin_bit_cast(bf16x8, kt[u][kq]), acc, 0, 0, 0);
+    float sc[4];
+    tile_scores<SK, KS>(a, kt[u], scale, qsc, ksc[u], sc);
     const int j = j0 + 16 * u + m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = j < ns && j * stride < vis_i[i];
-      if (4 * g4 + i < rows_here) krow[i][j] = ok ? max(ord_key(acc[i] * scale), 1u) : 0u;
+      if (4 * g4 + i < rows_here) krow[i][j] = ok ? max(ord_key(sc[i]), 1u) : 0u;
     }
   }
 }
@@ -661,16 +697,20 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
 // Row mapping of the candidate pass: query row r of a 16-row tile sits in MFMA row
 // 4 * (r % 4) + r / 4, so lane group g4 (lanes 16 g4 .. 16 g4 + 15) holds rows 4 i + g4 for
 // i = 0..3 and, with 4 or 8 query rows, every lane group holds valid rows for the same i.
-template <int D, bool PAGED, int NI>
+//
+// SK (reduced-byte indexer): positions are scored on the sketch, and each row keeps the
+// candidates for its min(cand_mult * k, visible) largest sketch scores.
+template <int D, bool PAGED, int NI, bool SK>
 __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
-    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
-    const int32_t* __restrict__ k_per_req, int k_max, const uint32_t* __restrict__ sample_keys,
-    float* __restrict__ region, int64_t score_stride, uint32_t* __restrict__ counts, int chunk,
-    int chunks) {
+    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
+    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult,
+    const uint32_t* __restrict__ sample_keys, float* __restrict__ region, int64_t score_stride,
+    uint32_t* __restrict__ counts, int chunk, int chunks) {
   extern __shared__ int lds_pages[];
   __shared__ uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
   __shared__ float th_s[16];
-  constexpr int KS = D / 32;
+  constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
+  constexpr int UNR = SK ? 2 * kScoreUnroll : kScoreUnroll;  // tiles per step: the same bytes in flight
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int mt = blockIdx.z;
@@ -703,24 +743,27 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       const int r = r0 + rl;
       const int t = r / G, gi = r - (r / G) * G;
       const int vis = L - T + t + 1;
+      const int kk = min(kb, max(vis, 0));
+      const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
       const float th = row_tau(sample_keys + (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples,
-                               vis, min(kb, max(vis, 0)), stride);
+                               vis, keep, stride);
       if (lane == 0) th_s[rl] = th;
     }
   }
 
-  bf16x8 a[KS];
+  uint4 a[KS];
   {
     const int rl = 4 * (m & 3) + (m >> 2);  // query row of MFMA row m
     const int r = r0 + rl;
     if (rl < rows_here) {
       const int t = r / G, gi = r - (r / G) * G;
-      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+      for (int j = 0; j < KS; ++j)
+        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
     } else {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
     }
   }
   __syncthreads();  // page ids and thresholds
@@ -742,6 +785,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
   // threshold, byte offset of the slot; ring head, staged count, written count
   int vis[4];
   float th[4];
+  float qsc[4];  // SK: the rows' scales
   uint32_t slot[4];
   int64_t grow[4];
   bool valid[4];
@@ -756,49 +800,51 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       grow[i] = ((int64_t)b * T + t) * Hq + (h * G + gi);
       vis[i] = L - T + t + 1;
       th[i] = th_s[rl];
+      qsc[i] = SK ? sk.q_scales[grow[i]] : 0.f;
     } else {
       grow[i] = 0;
       vis[i] = 0;
       th[i] = INFINITY;
+      qsc[i] = 0.f;
     }
     slot[i] = (uint32_t)(((valid[i] ? grow[i] - row_lo : 0) * score_stride) * 4 +
                          (int64_t)(c * kCandWaves + wave) * 128);
   }
 
-  // kScoreUnroll adjacent 16-position tiles per iteration; the next iteration's K loads while
-  // this one is scored (ping-pong, unconditional loads clamped to the range's last tile)
-  constexpr int kStep = 16 * kScoreUnroll;
+  // UNR adjacent 16-position tiles per iteration; the next iteration's K loads while this one
+  // is scored (ping-pong, unconditional loads clamped to the range's last tile)
+  constexpr int kStep = 16 * UNR;
   const int last = wend > wbeg ? (wend - 1) & ~15 : wbeg;
-  uint4 cur[kScoreUnroll][KS], nxt[kScoreUnroll][KS];
-  auto load_tiles = [&](int n0, uint4 (&dst)[kScoreUnroll][KS]) {
+  uint4 cur[UNR][KS], nxt[UNR][KS];
+  float csc[UNR], nsc[UNR];  // SK: the tiles' key scales (this lane's position)
+  auto load_tiles = [&](int n0, uint4 (&dst)[UNR][KS], float (&dsc)[UNR]) {
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int tile = min(n0 + u * 16, last);
       const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
-                          (int64_t)min(m, L - 1 - tile) * D + g4 * 8;
+                          (int64_t)min(m, L - 1 - tile) * D;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) dst[u][j] = ld16(kv.k + off + j * 32);
+      for (int j = 0; j < KS; ++j)
+        dst[u][j] = SK ? ld16i8(sk.codes + off + g4 * 16 + j * 64) : ld16(kv.k + off + g4 * 8 + j * 32);
+      dsc[u] = SK ? sk.scales[off / D] : 0.f;
     }
   };
   // Per tile and row: candidates s >= tau join the row's 32-entry LDS ring; once it holds 16, the
   // 16 from its head are written as one 128-byte line.
   // Tiles past the range (the second of a pair at the end) are scored on reloaded data and
   // keep nothing, so every iteration runs the same instructions.
-  auto score_tiles = [&](int n0, const uint4 (&kt)[kScoreUnroll][KS]) {
+  auto score_tiles = [&](int n0, const uint4 (&kt)[UNR][KS], const float (&ksc)[UNR]) {
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int tile = n0 + u * 16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kt[u][j]),
-                                                      acc, 0, 0, 0);
+      float sc[4];
+      tile_scores<SK, KS>(a, kt[u], scale, qsc, ksc[u], sc);
       const int n = tile + m;
       const bool in_range = n < wend;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         uint2* st = stage[wave][4 * i + g4];
-        const float s = acc[i] * scale;
+        const float s = sc[i];
         const bool pred = in_range && n < vis[i] && s >= th[i];
         const uint64_t mask = __ballot(pred);
         const uint32_t seg = (uint32_t)(mask >> (16 * g4)) & 0xffffu;
@@ -819,12 +865,12 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
   };
   if (wbeg < wend) {
     int n0 = wbeg;
-    load_tiles(n0, cur);
+    load_tiles(n0, cur, csc);
     do {
-      load_tiles(n0 + kStep, nxt);
-      score_tiles(n0, cur);
-      load_tiles(n0 + 2 * kStep, cur);
-      score_tiles(n0 + kStep, nxt);
+      load_tiles(n0 + kStep, nxt, nsc);
+      score_tiles(n0, cur, csc);
+      load_tiles(n0 + 2 * kStep, cur, csc);
+      score_tiles(n0 + kStep, nxt, nsc);
       n0 += 2 * kStep;
     } while (n0 < wend);
   }
@@ -1172,6 +1218,36 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
 }
 
 
+// Slot counts of the row's chunks that hold positions < L (nsub slots, each capped at cap) and
+// their exclusive prefix sums into prefix_s[0 .. kMaxCandSlots]; returns the total and sets
+// overflow when a slot lost candidates.  Ends with a barrier.
+__device__ uint32_t slot_prefix(const uint32_t* __restrict__ counts, int row, int chunks, int nsub,
+                                int cap, uint32_t* prefix_s, SelShared& sh, bool& overflow) {
+  const int tid = threadIdx.x;
+  constexpr int kPerT = kMaxCandSlots / kCsThreads;  // slots per thread
+  uint32_t cc[kPerT];
+  uint32_t local = 0;
+  bool over = false;
+#pragma unroll
+  for (int e = 0; e < kPerT; ++e) {
+    const int sidx = tid * kPerT + e;
+    const uint32_t cnt = sidx < nsub ? counts[(int64_t)row * chunks * kCandWaves + sidx] : 0u;
+    over |= cnt > (uint32_t)cap;
+    cc[e] = cnt > (uint32_t)cap ? (uint32_t)cap : cnt;
+    local += cc[e];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan<kCsWaves>(local, sh.wsum, &total);
+#pragma unroll
+  for (int e = 0; e < kPerT; ++e) {
+    prefix_s[tid * kPerT + e] = run;
+    run += cc[e];
+  }
+  if (tid == 0) prefix_s[kMaxCandSlots] = total;
+  overflow = __syncthreads_or(over) != 0;
+  return total;
+}
+
 // FUSED (the decode step): the selection also goes to the row's (position, score) list in
 // sel_pos / sel_score, the workgroup then attends to it (attend_list) and writes out / lse;
 // indices may then be nullptr.
@@ -1213,30 +1289,10 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     return;
   }
 
-  // ---- slot counts of the chunks holding positions < L, and their prefix sums
   const int cap = cand_cap(chunk);
   const int nsub = ((L + chunk - 1) / chunk) * kCandWaves;
-  constexpr int kPerT = kMaxCandSlots / kCsThreads;  // slots per thread
-  uint32_t cc[kPerT];
-  uint32_t local = 0;
-  bool over = false;
-#pragma unroll
-  for (int e = 0; e < kPerT; ++e) {
-    const int sidx = tid * kPerT + e;
-    const uint32_t cnt = sidx < nsub ? counts[(int64_t)row * chunks * kCandWaves + sidx] : 0u;
-    over |= cnt > (uint32_t)cap;
-    cc[e] = cnt > (uint32_t)cap ? (uint32_t)cap : cnt;
-    local += cc[e];
-  }
-  uint32_t total;
-  uint32_t run = block_excl_scan<kCsWaves>(local, sh.wsum, &total);
-#pragma unroll
-  for (int e = 0; e < kPerT; ++e) {
-    prefix_s[tid * kPerT + e] = run;
-    run += cc[e];
-  }
-  if (tid == 0) prefix_s[kMaxCandSlots] = total;
-  const bool overflow = __syncthreads_or(over) != 0;
+  bool overflow;
+  const uint32_t total = slot_prefix(counts, row, chunks, nsub, cap, prefix_s, sh, overflow);
 
   if (overflow || total < (uint32_t)kk) {
     // ---- exact fallback: every score of the row into its workspace area, then select
@@ -1267,6 +1323,157 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
   if constexpr (FUSED) {
     __syncthreads();  // the selected list is complete, LDS free again
     attend_list<D, PAGED>(kv, b, hq / G, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
+                          out + (int64_t)row * D, lse + row);
+  }
+}
+
+// ============================================================================ reduced-byte indexer
+// C of the sketch pipeline (A and B are sample_keys_kernel / score_cand_kernel with SK): per row,
+// the nc = min(cand_mult * k', visible) positions with the largest sketch scores (lower position
+// first among equal values) go to the row's list -- from the candidates, or from every sketch
+// score of the row when the candidates may not hold them (too few, or a slot overflowed), or
+// every visible position when nc = visible; the list entries then get their exact scores and
+// the k' largest of those (lower position first) are the selection.
+
+// A row's list in global memory, in position order, keyed by its scores.
+struct ListSource {
+  const int32_t* pos;
+  const float* score;
+  __device__ __forceinline__ uint32_t key(int f) const { return ord_key(score[f]); }
+  __device__ __forceinline__ void pos8(int f0, int total, uint32_t, uint32_t (&p)[kCsPer]) const {
+#pragma unroll
+    for (int e = 0; e < kCsPer; ++e) p[e] = f0 + e < total ? (uint32_t)pos[f0 + e] : 0u;
+  }
+};
+
+// Sketch score of every visible position of query row `qr` into srow: D / 16 lanes per position,
+// 16 codes each, integer dot products (v_dot4) summed exactly (every partial sum is an integer
+// below 2^24) -- the same values as the MFMA pass.
+template <int D, bool PAGED>
+__device__ void sketch_row_scores(const KVArgs& kv, const SketchArgs& sk, int b, int h, int64_t qr,
+                                  int vis, float* __restrict__ srow) {
+  constexpr int LPP = D / 16, PPW = kWave / LPP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = lane / LPP, c = lane - (lane / LPP) * LPP;
+  const uint4 qc = ld16i8(sk.q_codes + qr * D + c * 16);
+  const float qs = sk.q_scales[qr];
+  for (int n0 = wave * PPW; n0 < vis; n0 += kCsWaves * PPW) {
+    const int n = n0 + p;
+    const bool ok = n < vis;
+    const int64_t off = kv_row<D, PAGED>(kv, b, h, ok ? n : 0);
+    const uint4 kc = ld16i8(sk.codes + off + c * 16);
+    int d = 0;
+    d = __builtin_amdgcn_sdot4((int)qc.x, (int)kc.x, d, false);
+    d = __builtin_amdgcn_sdot4((int)qc.y, (int)kc.y, d, false);
+    d = __builtin_amdgcn_sdot4((int)qc.z, (int)kc.z, d, false);
+    d = __builtin_amdgcn_sdot4((int)qc.w, (int)kc.w, d, false);
+    const float dot = group_sum<LPP>((float)d);
+    if (ok && c == 0) srow[n] = (qs * sk.scales[off / D]) * dot;
+  }
+}
+
+// Exact scores of list entries [0, n) (positions pos[f], all visible) into score[f]: D / 8 lanes
+// per position, kRerankSteps positions per lane group with their loads in flight together.
+constexpr int kRerankSteps = 16;
+template <int D, bool PAGED>
+__device__ void rerank_exact(const KVArgs& kv, int b, int h, const uint16_t* __restrict__ qrow, float scale,
+                             const int32_t* __restrict__ pos, float* __restrict__ score, int n) {
+  constexpr int LPP = D / 8, PPW = kWave / LPP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = lane / LPP, c = lane - (lane / LPP) * LPP;
+  const uint4 qv = ld16(qrow + c * 8);
+  for (int base = wave * PPW * kRerankSteps; base < n; base += kCsWaves * PPW * kRerankSteps) {
+    int pp[kRerankSteps];
+#pragma unroll
+    for (int u = 0; u < kRerankSteps; ++u) pp[u] = pos[min(base + u * PPW + p, n - 1)];
+    uint4 kr[kRerankSteps];
+#pragma unroll
+    for (int u = 0; u < kRerankSteps; ++u) kr[u] = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, pp[u]) + c * 8);
+#pragma unroll
+    for (int u = 0; u < kRerankSteps; ++u) {
+      float dot = 0.f;
+      dot = dot2_bf16(qv.x, kr[u].x, dot);
+      dot = dot2_bf16(qv.y, kr[u].y, dot);
+      dot = dot2_bf16(qv.z, kr[u].z, dot);
+      dot = dot2_bf16(qv.w, kr[u].w, dot);
+      dot = group_sum<LPP>(dot);
+      const int f = base + u * PPW + p;
+      if (f < n && c == 0) score[f] = dot * scale;
+    }
+  }
+}
+
+// list_pos / list_score: the rows' lists (list_stride >= min(cand_mult * k_max, max_len) entries).
+// FUSED: as for cand_select_kernel, the selection also goes to sel_pos / sel_score and the row's
+// attention over it to out / lse.
+template <int D, bool PAGED, bool FUSED>
+__global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
+    const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
+    const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int cand_mult, int lds_cap,
+    int32_t* __restrict__ list_pos, float* __restrict__ list_score, int list_stride,
+    int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
+    float* __restrict__ out, float* __restrict__ lse) {
+  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
+  __shared__ SelShared sh;
+  __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
+  uint32_t* lds_key = smem;
+  uint32_t* hist = smem + lds_cap;
+  const int row = blockIdx.x;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  const int hq = row - (row / Hq) * Hq;
+  const int h = hq / G;
+  const int L = seq_len_of(kv, b);
+  const int vis = max(0, L - T + t + 1);
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, vis);
+  const int nc = (int)min((int64_t)cand_mult * kk, (int64_t)vis);
+  SelOut so;
+  so.idx = indices ? indices + (int64_t)row * k_max : nullptr;
+  so.pos = FUSED ? sel_pos + (int64_t)row * k_max : nullptr;
+  so.score = FUSED ? sel_score + (int64_t)row * k_max : nullptr;
+  const int tid = threadIdx.x;
+  if (kk == 0 || (!FUSED && kk == vis)) {
+    if (so.idx)
+      for (int i = tid; i < k_max; i += kCsThreads) so.idx[i] = i < kk ? i : -1;
+    if (FUSED) {
+      for (int i = tid; i < D; i += kCsThreads) out[(int64_t)row * D + i] = 0.f;
+      if (tid == 0) lse[row] = -INFINITY;
+    }
+    return;
+  }
+  int32_t* lpos = list_pos + (int64_t)row * list_stride;
+  float* lsc = list_score + (int64_t)row * list_stride;
+  if (nc == vis) {
+    for (int f = tid; f < vis; f += kCsThreads) lpos[f] = f;
+  } else {
+    const int cap = cand_cap(chunk);
+    const int nsub = ((L + chunk - 1) / chunk) * kCandWaves;
+    bool overflow;
+    const uint32_t total = slot_prefix(counts, row, chunks, nsub, cap, prefix_s, sh, overflow);
+    SelOut lo;
+    lo.idx = nullptr;
+    lo.pos = lpos;
+    lo.score = lsc;
+    if (overflow || total < (uint32_t)nc) {
+      float* srow = region + (int64_t)row * score_stride;
+      sketch_row_scores<D, PAGED>(kv, sk, b, h, row, vis, srow);
+      __syncthreads();
+      select_ordered(DenseSource{srow}, vis, nc, nc, lo, hist, sh);
+    } else {
+      cand_path(total, nsub, cap, lo, nc, nc, row, region, score_stride, chunks, prefix_s, lds_key,
+                lds_cap, hist, sh);
+    }
+  }
+  __syncthreads();  // the list is complete
+  rerank_exact<D, PAGED>(kv, b, h, q + (int64_t)row * D, scale, lpos, lsc, nc);
+  __syncthreads();
+  select_ordered(ListSource{lpos, lsc}, nc, kk, k_max, so, hist, sh);
+  if constexpr (FUSED) {
+    __syncthreads();  // the selected list is complete, LDS free again
+    attend_list<D, PAGED>(kv, b, h, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
                           out + (int64_t)row * D, lse + row);
   }
 }
@@ -1307,44 +1514,65 @@ static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool SK>
 static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   const int tiles = (a.GT + 15) / 16;
   const int groups = a.B * a.kv.num_kv_heads;
-  hipLaunchKernelGGL((sample_keys_kernel<D, PAGED>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
-                     0, stream, a.q, a.kv, a.T, a.Hq, a.G, a.scale, a.sample_keys);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if constexpr (SK) {
+    if ((e = launch_q_sketch(a.q, a.rows, D, a.sk.q_codes, a.sk.q_scales, stream)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((sample_keys_kernel<D, PAGED, SK>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
+                     0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.sample_keys);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
   const int rows_tile = a.GT < 16 ? a.GT : 16;
-  auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1>
-                             : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2> : score_cand_kernel<D, PAGED, 4>);
+  auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK>
+                             : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK> : score_cand_kernel<D, PAGED, 4, SK>);
   hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
-                     page_ids * sizeof(int), stream, a.q, a.kv, a.T, a.Hq, a.G, a.scale, a.k_per_req,
-                     a.k_max, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                     page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req,
+                     a.k_max, a.cand_mult, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
                      a.cand_chunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // candidate keys held in LDS: about kCandFactor * k expected, room for 4.5 k (at most 12288)
-  int lds_cap = (int)(((int64_t)a.k_max * 9 / 2 + 255) / 256 * 256);
+  // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
+  // the largest list (at most 12288)
+  const int64_t keep_max = SK ? (int64_t)a.list_stride : (int64_t)a.k_max;
+  int lds_cap = (int)((keep_max * 9 / 2 + 255) / 256 * 256);
   if (lds_cap > kCsMaxBlocks * kCsThreads * kCsPer) lds_cap = kCsMaxBlocks * kCsThreads * kCsPer;
   const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
-  auto sel = a.fused ? cand_select_kernel<D, PAGED, true> : cand_select_kernel<D, PAGED, false>;
-  if (lds > 65536) {
-    e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if constexpr (SK) {
+    auto sel = a.fused ? sketch_select_kernel<D, PAGED, true> : sketch_select_kernel<D, PAGED, false>;
+    if (lds > 65536) {
+      e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G,
+                       a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                       a.cand_chunks, a.k_max, a.cand_mult, lds_cap, a.list_pos, a.list_score,
+                       a.list_stride, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
+  } else {
+    auto sel = a.fused ? cand_select_kernel<D, PAGED, true> : cand_select_kernel<D, PAGED, false>;
+    if (lds > 65536) {
+      e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
+                       a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                       a.cand_chunks, a.k_max, lds_cap, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
   }
-  hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
-                     a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                     a.cand_chunks, a.k_max, lds_cap, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
   return hipGetLastError();
 }
 
+template <bool SK>
+static hipError_t launch_filtered(const TopkLaunch& a, hipStream_t stream) {
+  if (a.D == 128)
+    return a.paged ? launch_filtered_t<128, true, SK>(a, stream) : launch_filtered_t<128, false, SK>(a, stream);
+  return a.paged ? launch_filtered_t<64, true, SK>(a, stream) : launch_filtered_t<64, false, SK>(a, stream);
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
-  if (a.filtered) {
-    if (a.D == 128)
-      return a.paged ? launch_filtered_t<128, true>(a, stream) : launch_filtered_t<128, false>(a, stream);
-    return a.paged ? launch_filtered_t<64, true>(a, stream) : launch_filtered_t<64, false>(a, stream);
-  }
+  if (a.sketch) return launch_filtered<true>(a, stream);
+  if (a.filtered) return launch_filtered<false>(a, stream);
   hipError_t e = launch_fill_u32(a.hist, (int64_t)a.rows * kHistBins, 0u, stream);
   if (e != hipSuccess) return e;
   if (a.D == 128)

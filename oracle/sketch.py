@@ -33,7 +33,7 @@ import numpy as np
 
 from .reference import Cache, bf16_bits_to_f64, scaled_scores, visible_length
 
-__all__ = ["int8_sketch", "sketch_scores", "row_topk_sketch", "decode_topk_sketch"]
+__all__ = ["int8_sketch", "sketch_scores", "sketch_candidates", "row_topk_sketch", "decode_topk_sketch"]
 
 
 def int8_sketch(rows) -> Tuple[np.ndarray, np.ndarray]:
@@ -58,16 +58,26 @@ def sketch_scores(q_row, codes, scales) -> np.ndarray:
     return (prod * dot.astype(np.float32)).astype(np.float32)
 
 
+def sketch_candidates(q_row, keys, visible: int, k: int, cand_mult: int) -> np.ndarray:
+    """Ascending positions of the min(m * k', visible) visible keys with the largest sketch
+    scores (lower position first among equal values), k' = min(k, visible)."""
+    visible = max(0, min(int(visible), keys.shape[0]))
+    kk = max(0, min(int(k), visible))
+    nc = min(int(cand_mult) * kk, visible)
+    if nc == 0:
+        return np.zeros(0, dtype=np.int64)
+    codes, scales = int8_sketch(keys[:visible])
+    approx = sketch_scores(q_row, codes, scales)
+    return np.sort(np.argsort(-approx, kind="stable")[:nc])
+
+
 def row_topk_sketch(q_row, keys, visible: int, k: int, cand_mult: int, scale=None) -> np.ndarray:
     """Reduced-byte indexer for one row: ascending positions of the selection described above."""
     visible = max(0, min(int(visible), keys.shape[0]))
     kk = max(0, min(int(k), visible))
+    cand = sketch_candidates(q_row, keys, visible, kk, cand_mult)
     if kk == 0:
-        return np.zeros(0, dtype=np.int64)
-    nc = min(int(cand_mult) * kk, visible)
-    codes, scales = int8_sketch(keys[:visible])
-    approx = sketch_scores(q_row, codes, scales)
-    cand = np.sort(np.argsort(-approx, kind="stable")[:nc])
+        return cand
     s32 = scaled_scores(q_row, keys[cand], scale).astype(np.float32)
     keep = np.argsort(-s32, kind="stable")[:kk]
     return np.sort(cand[keep])

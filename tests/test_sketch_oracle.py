@@ -177,6 +177,7 @@ def test_selection_bruteforce_rank_counting(trial):
     approx = [float(np.float32(np.float32(qs[0]) * ks[i]) * np.float32(int(np.dot(qc[0].astype(int), kc[i].astype(int)))))
               for i in range(vis)]
     cand = _rank_count_select(approx, min(m * kk, vis), list(range(vis)))
+    assert oracle.sketch_candidates(q, K, vis, k, m).tolist() == cand
     exact = [float(np.float32(float(np.dot(q, K[i])) / math.sqrt(d))) for i in range(vis)]
     want = _rank_count_select(exact, kk, cand)
     assert got == want
