@@ -6,6 +6,10 @@
 A step is one pass of the whole hot path over one decode batch, on one stream:
     flush -> topk_index -> flush -> sparse_decode_attn -> flush -> dense_decode_attn
           -> flush -> sparse_decode_step (indexer + sparse attention in one call)
+          -> flush -> topk_index_sketch -> flush -> sparse_decode_step_sketch
+The last two run the reduced-byte indexer (int8 key sketch, cand_mult * k candidates re-ranked
+on exact scores) on a sketch built before the timed region; the per-step sketch update of the
+T new positions per request (key_sketch_build with last_n = T) is timed as its own call.
 `flush` reads a 2 GiB scratch buffer so that neither L2 nor the 256 MB Infinity Cache holds any
 KV bytes when a hot-path call starts (every call is measured from cold caches).  Each call is
 bracketed by HIP events recorded on the stream it runs on.  Inputs are seeded synthetic tensors
@@ -48,6 +52,12 @@ KERNEL_SOURCES = {
     "sparse_decode_step": ["long_context_sparse_oracle_amd/csrc/topk.hip",
                            "long_context_sparse_oracle_amd/csrc/attention.hip",
                            "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "topk_index_sketch": ["long_context_sparse_oracle_amd/csrc/topk.hip",
+                          "long_context_sparse_oracle_amd/csrc/sketch.hip",
+                          "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "sparse_decode_step_sketch": ["long_context_sparse_oracle_amd/csrc/topk.hip",
+                                  "long_context_sparse_oracle_amd/csrc/sketch.hip",
+                                  "long_context_sparse_oracle_amd/csrc/device_common.h"],
 }
 
 
@@ -66,6 +76,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--sweep-k", default=None, help="k for a sweep workload (s10/s50/s100/s500/s1000)")
+    p.add_argument("--cand-mult", type=int, default=2,
+                   help="candidates per selected position of the reduced-byte indexer")
     p.add_argument("--sparse-splits", type=int, default=0)
     p.add_argument("--dense-splits", type=int, default=0)
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the reported figure)")
@@ -76,7 +88,7 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(wl, idx):
+def algorithmic_bytes(wl, idx, cand_mult):
     """Bytes the method must move per call (d-dim bf16 rows, int32 indices, fp32 outputs)."""
     import torch
 
@@ -103,7 +115,44 @@ def algorithmic_bytes(wl, idx):
         "topk": tokens * Hkv * row_bytes + index_bytes + q_bytes,
         # the one-call step: all of K once (scores), V of the distinct selected rows, q, outputs
         "step": tokens * Hkv * row_bytes + distinct * row_bytes + q_bytes + o_bytes,
+        # reduced-byte indexer: every position's codes and scale once per KV head, then each row's
+        # min(cand_mult * k', visible) candidate K rows for the exact re-rank
+        "sketch_topk": tokens * Hkv * (d + 4) + rerank_rows(wl, cand_mult) * row_bytes + index_bytes + q_bytes,
+        "sketch_step": tokens * Hkv * (d + 4) + rerank_rows(wl, cand_mult) * row_bytes + distinct * row_bytes
+                       + q_bytes + o_bytes,
+        "rerank_rows": rerank_rows(wl, cand_mult),
     }
+
+
+def rerank_rows(wl, cand_mult):
+    """K rows the re-rank of the reduced-byte indexer reads: min(cand_mult * k', visible) per row."""
+    total = 0
+    lens = wl.seq_lens.tolist()
+    kreq = wl.k_per_req.tolist()
+    for b in range(wl.batch):
+        for t in range(wl.q_len):
+            vis = max(0, lens[b] - wl.q_len + t + 1)
+            kk = min(min(kreq[b], wl.k_max), vis)
+            total += min(cand_mult * kk, vis) * wl.num_q_heads
+    return total
+
+
+def recall(idx_a, idx_b, max_len):
+    """Fraction of idx_b's entries (>= 0) that idx_a's row also holds."""
+    import torch
+
+    rows = idx_a.shape[0] * idx_a.shape[1] * idx_a.shape[2]
+    a = idx_a.reshape(rows, -1).long()
+    bb = idx_b.reshape(rows, -1).long()
+    hit = 0
+    for r0 in range(0, rows, 256):
+        ma = torch.zeros((min(256, rows - r0), max_len + 1), dtype=torch.bool, device=a.device)
+        ma.scatter_(1, torch.where(a[r0:r0 + 256] < 0, max_len, a[r0:r0 + 256]), True)
+        ma[:, max_len] = False
+        vb = bb[r0:r0 + 256]
+        hit += int(torch.gather(ma, 1, torch.where(vb < 0, max_len, vb)).sum())
+    total = int((bb >= 0).sum())
+    return hit / total if total else 1.0
 
 
 def cpu_baseline(wl, gathered_bytes, seconds):
@@ -274,6 +323,17 @@ def main():
     lse_st = torch.empty_like(lse_s)
     ws_st = torch.empty(max(1, cs.sparse_decode_step_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8,
                         device=dev)
+    # reduced-byte indexer: the sketch of every cached key, built once (in serving it is kept up to
+    # date by sketching each step's new positions, the timed `key_sketch_update` call)
+    m = args.cand_mult
+    sketch = cs.key_sketch_build(cache)
+    idx_sk = torch.empty_like(indices)
+    ws_tk = torch.empty(max(1, cs.topk_index_sketch_workspace_size(wl.q, cache, k_max, m)), dtype=torch.uint8,
+                        device=dev)
+    out_sk = torch.empty_like(out_s)
+    lse_sk = torch.empty_like(lse_s)
+    ws_sk = torch.empty(max(1, cs.sparse_decode_step_sketch_workspace_size(wl.q, cache, k_max, m)),
+                        dtype=torch.uint8, device=dev)
     # cache flush by reading 2 GiB: evicts every KV line from L2 and the Infinity Cache and leaves
     # clean lines behind (a write flush would leave dirty lines whose write-back the next call
     # would pay for)
@@ -293,6 +353,12 @@ def main():
                                                           out=out_d, lse=lse_d, workspace=ws_d),
         "sparse_decode_step": lambda: cs.sparse_decode_step(wl.q, cache, kptr, k_max=k_max, out=out_st,
                                                             lse=lse_st, workspace=ws_st),
+        "key_sketch_update": lambda: cs.key_sketch_build(cache, sketch, last_n=T),
+        "topk_index_sketch": lambda: cs.topk_index_sketch(wl.q, cache, sketch, kptr, k_max=k_max, cand_mult=m,
+                                                          indices=idx_sk, workspace=ws_tk),
+        "sparse_decode_step_sketch": lambda: cs.sparse_decode_step_sketch(wl.q, cache, sketch, kptr, k_max=k_max,
+                                                                          cand_mult=m, out=out_sk, lse=lse_sk,
+                                                                          workspace=ws_sk),
     }
     times = {k: [] for k in calls}
 
@@ -339,7 +405,20 @@ def main():
         hev.destroy(e0)
         hev.destroy(e1)
 
-    ab = algorithmic_bytes(wl, indices)
+    ab = algorithmic_bytes(wl, indices, m)
+    # one full build of the sketch (every cached key), timed on its own after the steps
+    hev2 = HipEvents()
+    eb0, eb1 = hev2.create(), hev2.create()
+    flush()
+    hev2.record(eb0, sh)
+    cs.key_sketch_build(cache, sketch)
+    hev2.record(eb1, sh)
+    torch.cuda.synchronize()
+    build_us = hev2.elapsed_us(eb0, eb1)
+    hev2.destroy(eb0)
+    hev2.destroy(eb1)
+    sk_recall = recall(idx_sk, indices, wl.max_len)
+    sk_out_diff = float((out_sk - out_st).abs().max())
     mean = {k: statistics.fmean(v) for k, v in times.items()}
     med = {k: statistics.median(v) for k, v in times.items()}
     traffic = load_traffic()
@@ -383,11 +462,25 @@ def main():
         "e2e_speedup_vs_dense": round(mean["dense_decode_attn"] / (mean["topk_index"] + mean["sparse_decode_attn"]), 3),
         "step_us": round(mean["sparse_decode_step"], 2),
         "step_speedup_vs_dense": round(mean["dense_decode_attn"] / mean["sparse_decode_step"], 3),
+        "sketch": {
+            "cand_mult": m,
+            "topk_us": round(mean["topk_index_sketch"], 2),
+            "step_us": round(mean["sparse_decode_step_sketch"], 2),
+            "update_us": round(mean["key_sketch_update"], 2),
+            "step_speedup_vs_dense": round(mean["dense_decode_attn"] /
+                                           (mean["sparse_decode_step_sketch"] + mean["key_sketch_update"]), 3),
+            "full_build_us": round(build_us, 2),
+            "recall_vs_exact_topk": round(sk_recall, 5),
+            "max_abs_out_diff_vs_exact_step": sk_out_diff,
+            "rerank_rows": ab["rerank_rows"],
+        },
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
         "algorithmic_bytes": {"topk_index": ab["topk"], "sparse_decode_attn": ab["sparse"],
-                              "dense_decode_attn": ab["dense"], "sparse_decode_step": ab["step"]},
+                              "dense_decode_attn": ab["dense"], "sparse_decode_step": ab["step"],
+                              "topk_index_sketch": ab["sketch_topk"],
+                              "sparse_decode_step_sketch": ab["sketch_step"]},
         "distinct_rows": ab["distinct_rows"],
         "selected_rows": ab["selected_rows"],
         "roofline": roofline("sparse_decode_attn", ab["sparse"]),
@@ -395,6 +488,8 @@ def main():
             "topk_index": roofline("topk_index", ab["topk"]),
             "dense_decode_attn": roofline("dense_decode_attn", ab["dense"]),
             "sparse_decode_step": roofline("sparse_decode_step", ab["step"]),
+            "topk_index_sketch": roofline("topk_index_sketch", ab["sketch_topk"]),
+            "sparse_decode_step_sketch": roofline("sparse_decode_step_sketch", ab["sketch_step"]),
         },
     }
     if args.cpu_seconds > 0:

@@ -168,8 +168,14 @@ cs_status check_sketch(const cs_key_sketch* sk) {
 // keys, slot counts, the query rows' codes and scales, the candidate lists (positions, scores),
 // then the selected lists of the step.
 struct SketchWs {
-  size_t scores, keys, counts, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
+  size_t scores, hist, keys, counts, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
 };
+
+// Lists longer than 1/16 of the cache come from every sketch score (the candidate slots hold
+// about half of a chunk's positions).
+bool sketch_full(const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
+  return (int64_t)cand_mult * k_max * 16 > kv->max_len;
+}
 
 SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult,
                           bool step) {
@@ -179,7 +185,8 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
   const size_t ls = (size_t)sketch_list_stride(kv, k_max, cand_mult);
   SketchWs w;
   w.scores = 0;
-  w.keys = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.keys = w.hist + (sketch_full(kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
   w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
   w.q_codes = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
@@ -304,6 +311,7 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   cs::TopkLaunch a;
   a.fused = false;
   a.sketch = false;
+  a.sketch_full = false;
   a.sk = cs::SketchArgs{nullptr, nullptr, nullptr, nullptr};
   a.cand_mult = 1;
   a.list_pos = nullptr;
@@ -530,7 +538,8 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
   a.sk.q_codes = reinterpret_cast<int8_t*>(ws + lay.q_codes);
   a.sk.q_scales = reinterpret_cast<float*>(ws + lay.q_scales);
   a.scores = reinterpret_cast<float*>(ws + lay.scores);
-  a.hist = nullptr;
+  a.sketch_full = sketch_full(kv, k_max, cand_mult);
+  a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);

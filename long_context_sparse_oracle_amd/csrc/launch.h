@@ -49,6 +49,7 @@ struct TopkLaunch {
   // reduced-byte indexer: candidates ranked on the sketch, cand_mult * k of them re-ranked on
   // exact scores through the list area (positions and scores, list_stride entries per row)
   bool sketch;
+  bool sketch_full;  // lists from every sketch score (score + histogram, select) instead of candidates
   SketchArgs sk;
   int cand_mult;
   int32_t* list_pos;

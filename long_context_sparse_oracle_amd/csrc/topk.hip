@@ -30,6 +30,35 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t va
   for (; i < n / 4; i += stride) p4[i] = v;
 }
 
+// 16 bytes of int8 codes
+__device__ __forceinline__ uint4 ld16i8(const int8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Scores of one 16-position tile for the 4 MFMA rows 4 * (lane / 16) + i of this lane, from the
+// operand steps a (query rows) and kt (key rows, this lane's position lane % 16):
+//   exact   bf16 dot products times `scale`;
+//   SK      sketch scores (qsc[i] * ksc) * (c_q . c_k), the integer dot product exact in int32.
+template <bool SK, int KS>
+__device__ __forceinline__ void tile_scores(const uint4 (&a)[KS], const uint4 (&kt)[KS], float scale,
+                                            const float (&qsc)[4], float ksc, float (&sc)[4]) {
+  if constexpr (SK) {
+    i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]), __builtin_bit_cast(i32x4, kt[j]),
+                                                  acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (qsc[i] * ksc) * (float)acc[i];
+  } else {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]), __builtin_bit_cast(bf16x8, kt[j]),
+                                                    acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = acc[i] * scale;
+  }
+}
+
 // ============================================================================ score + histogram
 // Grid: (chunks, B * Hkv, ceil(G*T / 16)).  One workgroup (4 waves per 4 query rows, so the
 // LDS histogram never starves a CU of waves) streams `chunk` positions of one (request, KV head)
@@ -39,14 +68,15 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t va
 // position l%16, the same 8 dims), so each K row is read once for all rows of the group.
 // Scores of visible positions go to scores[row][n]; their 12-bit key prefix is counted in an LDS
 // histogram (two 16-bit counters per word) that is added to the global one at the end.
-template <int D, bool PAGED>
+// SK: sketch scores instead (int8 codes of q and K, v_mfma_i32_16x16x64_i8).
+template <int D, bool PAGED, bool SK>
 __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
-    const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
+    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
     float* __restrict__ scores, uint32_t* __restrict__ hist, int chunk, int hist_rows,
     int64_t score_stride) {
   extern __shared__ uint32_t lds_hist[];  // [hist_rows][kHistBins / 2], then the chunk's page ids
   int* lds_pages = reinterpret_cast<int*>(lds_hist + hist_rows * (kHistBins / 2));
-  constexpr int KS = D / 32;              // MFMA k-steps per tile
+  constexpr int KS = SK ? D / 64 : D / 32;  // MFMA k-steps per tile
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int mt = blockIdx.z;
@@ -68,34 +98,39 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
   const int m = lane & 15;
   const int g4 = lane >> 4;
 
-  // A operand: query row r0 + m, dims j*32 + g4*8 .. +8.
-  bf16x8 a[KS];
+  // A operand: query row r0 + m, dims j*32 + g4*8 .. +8 (SK: codes j*64 + g4*16 .. +16).
+  uint4 a[KS];
   {
     const int r = r0 + m;
     if (r < GT) {
       const int t = r / G, gi = r - (r / G) * G;
-      const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + (h * G + gi)) * D + g4 * 8;
+      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, ld16(qp + j * 32));
+      for (int j = 0; j < KS; ++j)
+        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
     } else {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
     }
   }
   // Output rows held by this lane: 4*g4 + i (i = 0..3).
   int vis[4];
   float* srow[4];
+  float qsc[4];  // SK: the rows' scales
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = 4 * g4 + i;
     const int r = r0 + rl;
     if (rl < rows_here) {
       const int t = r / G, gi = r - (r / G) * G;
+      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
       vis[i] = L - T + t + 1;
-      srow[i] = scores + (((int64_t)b * T + t) * Hq + (h * G + gi)) * score_stride;
+      srow[i] = scores + qr * score_stride;
+      qsc[i] = SK ? sk.q_scales[qr] : 0.f;
     } else {
       vis[i] = 0;
       srow[i] = scores;
+      qsc[i] = 0.f;
     }
   }
   __syncthreads();
@@ -110,31 +145,31 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
   const int kStep = (int)(blockDim.x >> 6) * 16 * kScoreUnroll;
   const int last = (end - 1) & ~15;
   uint4 cur[kScoreUnroll][KS], nxt[kScoreUnroll][KS];
-  auto load_tiles = [&](int n0, uint4 (&dst)[kScoreUnroll][KS]) {
+  float csc[kScoreUnroll], nsc[kScoreUnroll];  // SK: the tiles' key scales (this lane's position)
+  auto load_tiles = [&](int n0, uint4 (&dst)[kScoreUnroll][KS], float (&dsc)[kScoreUnroll]) {
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
       const int tile = min(n0 + u * 16, last);
       const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
-                          (int64_t)min(m, L - 1 - tile) * D + g4 * 8;
+                          (int64_t)min(m, L - 1 - tile) * D;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) dst[u][j] = ld16(kbase + off + j * 32);
+      for (int j = 0; j < KS; ++j)
+        dst[u][j] = SK ? ld16i8(sk.codes + off + g4 * 16 + j * 64) : ld16(kbase + off + g4 * 8 + j * 32);
+      dsc[u] = SK ? sk.scales[off / D] : 0.f;
     }
   };
-  auto score_tiles = [&](int n0, const uint4 (&kt)[kScoreUnroll][KS]) {
+  auto score_tiles = [&](int n0, const uint4 (&kt)[kScoreUnroll][KS], const float (&ksc)[kScoreUnroll]) {
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
       const int tile = n0 + u * 16;
       if (tile >= end) break;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8, kt[u][j]),
-                                                      acc, 0, 0, 0);
+      float sc[4];
+      tile_scores<SK, KS>(a, kt[u], scale, qsc, ksc[u], sc);
       const int n = tile + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (n < vis[i]) {
-          const float s = acc[i] * scale;
+          const float s = sc[i];
           srow[i][n] = s;
           const uint32_t bin = ord_key(s) >> 20;
           atomicAdd(&lds_hist[(4 * g4 + i) * (kHistBins / 2) + (bin >> 1)], 1u << ((bin & 1u) * 16));
@@ -143,13 +178,13 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
     }
   };
   int n0 = start + wave * 16 * kScoreUnroll;
-  load_tiles(n0, cur);
+  load_tiles(n0, cur, csc);
   for (; n0 < end; n0 += 2 * kStep) {
-    load_tiles(n0 + kStep, nxt);
-    score_tiles(n0, cur);
+    load_tiles(n0 + kStep, nxt, nsc);
+    score_tiles(n0, cur, csc);
     if (n0 + kStep >= end) break;
-    load_tiles(n0 + 2 * kStep, cur);
-    score_tiles(n0 + kStep, nxt);
+    load_tiles(n0 + 2 * kStep, cur, csc);
+    score_tiles(n0 + kStep, nxt, nsc);
   }
   __syncthreads();
 
@@ -486,12 +521,14 @@ __device__ void select_dense_row(const float* __restrict__ srow, const uint32_t*
   emit_selection(l, words, need, take_all_eq, kk, k_max, out, sh);
 }
 
-// One workgroup per row (b, t, hq): the kk = min(k_b, visible) largest scores of the row, from
-// the scores and histogram of score_hist_kernel.
+// One workgroup per row (b, t, hq): the min(mult * k', visible) largest scores of the row
+// (k' = min(k_b, visible); mult = 1 for the top-k itself), from the scores and histogram of
+// score_hist_kernel, into rows of out_stride entries.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_req, int T, int Hq,
-    int max_len, int64_t score_stride, int k_max, int bitmap_words, int32_t* __restrict__ indices) {
+    int max_len, int64_t score_stride, int k_max, int mult, int out_stride, int bitmap_words,
+    int32_t* __restrict__ indices) {
   extern __shared__ uint32_t smem[];
   __shared__ SelShared sh;
   const int row = blockIdx.x;
@@ -502,14 +539,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int vis = max(0, L - T + t + 1);
   int kb = k_per_req ? k_per_req[b] : k_max;
   kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
-  const int kk = min(kb, vis);
-  int32_t* out = indices + (int64_t)row * k_max;
+  const int kk = (int)min((int64_t)mult * min(kb, vis), (int64_t)vis);
+  int32_t* out = indices + (int64_t)row * out_stride;
   if (kk == vis || kk == 0) {  // everything visible is selected, or nothing
-    for (int i = threadIdx.x; i < k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
+    for (int i = threadIdx.x; i < out_stride; i += kSelThreads) out[i] = i < kk ? i : -1;
     return;
   }
   select_dense_row(scores + (int64_t)row * score_stride, hist + (int64_t)row * kHistBins, vis, kk,
-                   k_max, out, sel_lds(smem, bitmap_words), sh);
+                   out_stride, out, sel_lds(smem, bitmap_words), sh);
 }
 
 // ============================================================================ filtered indexer
@@ -534,35 +571,6 @@ constexpr int kTauParts = 4;                                       // workgroups
 constexpr int kTauWaves = 4;
 constexpr int kTauTilesPerWave = kTauSamples / kTauParts / 16 / kTauWaves;  // 4
 static_assert(kTauTilesPerWave * 16 * kTauWaves * kTauParts == kTauSamples, "sample tiling");
-
-// 16 bytes of int8 codes
-__device__ __forceinline__ uint4 ld16i8(const int8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// Scores of one 16-position tile for the 4 MFMA rows 4 * (lane / 16) + i of this lane, from the
-// operand steps a (query rows) and kt (key rows, this lane's position lane % 16):
-//   exact   bf16 dot products times `scale`;
-//   SK      sketch scores (qsc[i] * ksc) * (c_q . c_k), the integer dot product exact in int32.
-template <bool SK, int KS>
-__device__ __forceinline__ void tile_scores(const uint4 (&a)[KS], const uint4 (&kt)[KS], float scale,
-                                            const float (&qsc)[4], float ksc, float (&sc)[4]) {
-  if constexpr (SK) {
-    i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]), __builtin_bit_cast(i32x4, kt[j]),
-                                                  acc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (qsc[i] * ksc) * (float)acc[i];
-  } else {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]), __builtin_bit_cast(bf16x8, kt[j]),
-                                                    acc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = acc[i] * scale;
-  }
-}
 
 // Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
 __device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L + kTauSamples - 1) / kTauSamples : 1; }
@@ -886,7 +894,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
 }
 
 // ---- C: selection over a position-ordered list of (position, key) items
-constexpr int kCsThreads = 256;
+constexpr int kCsThreads = 512;
 constexpr int kCsWaves = kCsThreads / kWave;
 constexpr int kMaxCandSlots = (262144 / 1024) * kCandWaves;  // chunks of >= 1024 positions
 constexpr int kCsPer = 8;  // consecutive items per thread in the ordered passes
@@ -948,7 +956,7 @@ struct DenseSource {
   }
 };
 
-constexpr int kCsMaxBlocks = 6;  // candidate blocks of kCsThreads * kCsPer held with positions in registers
+constexpr int kCsMaxBlocks = 3;  // candidate blocks of kCsThreads * kCsPer held with positions in registers
 
 // Finds the kk-th largest key of the list (kmin <= every key <= kmax) by radix select over the
 // bits below their common prefix, in digits of up to 11 bits; hist holds 2048 counters.
@@ -1035,12 +1043,13 @@ __device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&k
 
 // Writes, in list order, the kk items of the largest keys (ties at the k-th key: earliest items)
 // and pads out to k_max with -1.  Keys and positions come from src (list in global memory).
+// kmin / kmax: bounds of the keys, when known.
 template <class Src>
 __device__ void select_ordered(const Src& src, int total, int kk, int k_max, const SelOut& so,
-                               uint32_t* hist, SelShared& sh) {
+                               uint32_t* hist, SelShared& sh, uint32_t kmin = 0u, uint32_t kmax = 0xffffffffu) {
   const int tid = threadIdx.x;
   uint32_t need, cnt_eq;
-  const uint32_t kstar = radix_kth([&](int f) { return src.key(f); }, total, kk, 0u, 0xffffffffu, hist, sh,
+  const uint32_t kstar = radix_kth([&](int f) { return src.key(f); }, total, kk, kmin, kmax, hist, sh,
                                    need, cnt_eq);
   const bool take_all_eq = cnt_eq == need;
   uint32_t eq_base = 0, out_base = 0;
@@ -1335,11 +1344,13 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
 // every visible position when nc = visible; the list entries then get their exact scores and
 // the k' largest of those (lower position first) are the selection.
 
-// A row's list in global memory, in position order, keyed by its scores.
+// A row's list in position order: positions in global memory, keys in LDS (key_lds) or from the
+// scores in global memory.
 struct ListSource {
   const int32_t* pos;
   const float* score;
-  __device__ __forceinline__ uint32_t key(int f) const { return ord_key(score[f]); }
+  const uint32_t* key_lds;
+  __device__ __forceinline__ uint32_t key(int f) const { return key_lds ? key_lds[f] : ord_key(score[f]); }
   __device__ __forceinline__ void pos8(int f0, int total, uint32_t, uint32_t (&p)[kCsPer]) const {
 #pragma unroll
     for (int e = 0; e < kCsPer; ++e) p[e] = f0 + e < total ? (uint32_t)pos[f0 + e] : 0u;
@@ -1372,25 +1383,31 @@ __device__ void sketch_row_scores(const KVArgs& kv, const SketchArgs& sk, int b,
   }
 }
 
-// Exact scores of list entries [0, n) (positions pos[f], all visible) into score[f]: D / 8 lanes
-// per position, kRerankSteps positions per lane group with their loads in flight together.
-constexpr int kRerankSteps = 16;
+// Exact scores of list entries [0, n) (positions pos[f], all visible): each wave takes kWave
+// entries per round, D / 8 lanes per entry (D / 8 entries per lane group, their K loads in flight
+// together); a round's positions arrive with one coalesced load, issued a round ahead, and are
+// spread by lane shuffles.  The ordered keys go to key_lds[f] when it is set, else the scores to
+// score[f]; the keys' bounds to sh.kmin / sh.kmax (initialised by the caller).
 template <int D, bool PAGED>
 __device__ void rerank_exact(const KVArgs& kv, int b, int h, const uint16_t* __restrict__ qrow, float scale,
-                             const int32_t* __restrict__ pos, float* __restrict__ score, int n) {
-  constexpr int LPP = D / 8, PPW = kWave / LPP;
+                             const int32_t* __restrict__ pos, float* __restrict__ score,
+                             uint32_t* key_lds, int n, SelShared& sh) {
+  constexpr int LPP = D / 8, PPW = kWave / LPP, NSTEP = kWave / PPW;
+  constexpr int kRound = kCsWaves * kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = lane / LPP, c = lane - (lane / LPP) * LPP;
   const uint4 qv = ld16(qrow + c * 8);
-  for (int base = wave * PPW * kRerankSteps; base < n; base += kCsWaves * PPW * kRerankSteps) {
-    int pp[kRerankSteps];
+  uint32_t lmin = 0xffffffffu, lmax = 0u;
+  int base = wave * kWave;
+  int my = base < n ? pos[min(base + lane, n - 1)] : 0;
+  for (; base < n; base += kRound) {
+    const int nb = base + kRound;
+    const int nxt = nb < n ? pos[min(nb + lane, n - 1)] : 0;
+    uint4 kr[NSTEP];
 #pragma unroll
-    for (int u = 0; u < kRerankSteps; ++u) pp[u] = pos[min(base + u * PPW + p, n - 1)];
-    uint4 kr[kRerankSteps];
+    for (int u = 0; u < NSTEP; ++u) kr[u] = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, __shfl(my, u * PPW + p)) + c * 8);
 #pragma unroll
-    for (int u = 0; u < kRerankSteps; ++u) kr[u] = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, pp[u]) + c * 8);
-#pragma unroll
-    for (int u = 0; u < kRerankSteps; ++u) {
+    for (int u = 0; u < NSTEP; ++u) {
       float dot = 0.f;
       dot = dot2_bf16(qv.x, kr[u].x, dot);
       dot = dot2_bf16(qv.y, kr[u].y, dot);
@@ -1398,12 +1415,22 @@ __device__ void rerank_exact(const KVArgs& kv, int b, int h, const uint16_t* __r
       dot = dot2_bf16(qv.w, kr[u].w, dot);
       dot = group_sum<LPP>(dot);
       const int f = base + u * PPW + p;
-      if (f < n && c == 0) score[f] = dot * scale;
+      if (f < n && c == 0) {
+        const float sc = dot * scale;
+        const uint32_t key = ord_key(sc);
+        lmin = min(lmin, key);
+        lmax = max(lmax, key);
+        if (key_lds) key_lds[f] = key; else score[f] = sc;
+      }
     }
+    my = nxt;
   }
+  atomicMin(&sh.kmin, lmin);
+  atomicMax(&sh.kmax, lmax);
 }
 
-// list_pos / list_score: the rows' lists (list_stride >= min(cand_mult * k_max, max_len) entries).
+// list_pos / list_score: the rows' lists (list_stride >= min(cand_mult * k_max, max_len) entries);
+// with `listed` the positions are already there (select_kernel over every sketch score).
 // FUSED: as for cand_select_kernel, the selection also goes to sel_pos / sel_score and the row's
 // attention over it to out / lse.
 template <int D, bool PAGED, bool FUSED>
@@ -1411,7 +1438,7 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
     const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
     const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int cand_mult, int lds_cap,
-    int32_t* __restrict__ list_pos, float* __restrict__ list_score, int list_stride,
+    int32_t* __restrict__ list_pos, float* __restrict__ list_score, int list_stride, bool listed,
     int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
     float* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
@@ -1446,31 +1473,43 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
   }
   int32_t* lpos = list_pos + (int64_t)row * list_stride;
   float* lsc = list_score + (int64_t)row * list_stride;
-  if (nc == vis) {
+  if (listed) {
+    // the list is in place
+  } else if (nc == vis) {
     for (int f = tid; f < vis; f += kCsThreads) lpos[f] = f;
   } else {
     const int cap = cand_cap(chunk);
     const int nsub = ((L + chunk - 1) / chunk) * kCandWaves;
     bool overflow;
     const uint32_t total = slot_prefix(counts, row, chunks, nsub, cap, prefix_s, sh, overflow);
+    // index lists only, one candidate per selected position (cand_mult = 1): the list is the
+    // selection, written straight to the row's indices
+    const bool direct = !FUSED && nc == kk;
     SelOut lo;
-    lo.idx = nullptr;
-    lo.pos = lpos;
-    lo.score = lsc;
+    lo.idx = direct ? so.idx : nullptr;
+    lo.pos = direct ? nullptr : lpos;
+    lo.score = direct ? nullptr : lsc;
+    const int lk = direct ? k_max : nc;
     if (overflow || total < (uint32_t)nc) {
       float* srow = region + (int64_t)row * score_stride;
       sketch_row_scores<D, PAGED>(kv, sk, b, h, row, vis, srow);
       __syncthreads();
-      select_ordered(DenseSource{srow}, vis, nc, nc, lo, hist, sh);
+      select_ordered(DenseSource{srow}, vis, nc, lk, lo, hist, sh);
     } else {
-      cand_path(total, nsub, cap, lo, nc, nc, row, region, score_stride, chunks, prefix_s, lds_key,
+      cand_path(total, nsub, cap, lo, nc, lk, row, region, score_stride, chunks, prefix_s, lds_key,
                 lds_cap, hist, sh);
     }
+    if (direct) return;
+  }
+  if (tid == 0) {
+    sh.kmin = 0xffffffffu;
+    sh.kmax = 0u;
   }
   __syncthreads();  // the list is complete
-  rerank_exact<D, PAGED>(kv, b, h, q + (int64_t)row * D, scale, lpos, lsc, nc);
+  uint32_t* rkey = nc <= lds_cap ? lds_key : nullptr;  // exact keys in LDS when they fit
+  rerank_exact<D, PAGED>(kv, b, h, q + (int64_t)row * D, scale, lpos, lsc, rkey, nc, sh);
   __syncthreads();
-  select_ordered(ListSource{lpos, lsc}, nc, kk, k_max, so, hist, sh);
+  select_ordered(ListSource{lpos, lsc, rkey}, nc, kk, k_max, so, hist, sh, sh.kmin, sh.kmax);
   if constexpr (FUSED) {
     __syncthreads();  // the selected list is complete, LDS free again
     attend_list<D, PAGED>(kv, b, h, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
@@ -1498,22 +1537,44 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
   return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool SK>
 static hipError_t launch_score_t(const TopkLaunch& a, hipStream_t stream) {
   const int rows_tile = a.GT < 16 ? a.GT : 16;
   const size_t page_ids = PAGED ? (size_t)(a.chunk >> a.kv.page_shift) + 2 : 0;
   const size_t lds = (size_t)rows_tile * (kHistBins / 2) * sizeof(uint32_t) + page_ids * sizeof(int);
-  auto kern = score_hist_kernel<D, PAGED>;
+  auto kern = score_hist_kernel<D, PAGED, SK>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.chunks, a.B * a.kv.num_kv_heads, (a.GT + 15) / 16);
-  hipLaunchKernelGGL(kern, grid, dim3(score_threads(a.GT)), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
+  hipLaunchKernelGGL(kern, grid, dim3(score_threads(a.GT)), lds, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G,
                      a.scale, a.scores, a.hist, a.chunk, rows_tile, a.score_stride);
   return hipGetLastError();
 }
 
+// Full-score path: every visible position's score (SK: sketch score) and the rows' histograms,
+// then the min(mult * k', visible) largest per row into `out` (rows of out_stride entries).
+template <int D, bool PAGED, bool SK>
+static hipError_t launch_full_select_t(const TopkLaunch& a, int mult, int out_stride, int32_t* out,
+                                       hipStream_t stream) {
+  hipError_t e = launch_fill_u32(a.hist, (int64_t)a.rows * kHistBins, 0u, stream);
+  if (e != hipSuccess) return e;
+  if ((e = launch_score_t<D, PAGED, SK>(a, stream)) != hipSuccess) return e;
+  const size_t lds = select_lds_bytes(a.kv.max_len);
+  if (lds > 65536) {
+    e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int words = ((a.kv.max_len + 255) / 256) * 8;
+  hipLaunchKernelGGL(select_kernel, dim3(a.rows), dim3(kSelThreads), lds, stream, a.scores,
+                     a.hist, a.kv.seq_lens, a.k_per_req, a.T, a.Hq, a.kv.max_len, a.score_stride,
+                     a.k_max, mult, out_stride, words, out);
+  return hipGetLastError();
+}
+
+// Candidate pipeline (A, B, C above); SK: the reduced-byte indexer, whose lists come from the
+// full-score path instead when a.sketch_full is set.
 template <int D, bool PAGED, bool SK>
 static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   const int tiles = (a.GT + 15) / 16;
@@ -1522,18 +1583,26 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   if constexpr (SK) {
     if ((e = launch_q_sketch(a.q, a.rows, D, a.sk.q_codes, a.sk.q_scales, stream)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((sample_keys_kernel<D, PAGED, SK>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
-                     0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.sample_keys);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
-  const int rows_tile = a.GT < 16 ? a.GT : 16;
-  auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK>
-                             : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK> : score_cand_kernel<D, PAGED, 4, SK>);
-  hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
-                     page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req,
-                     a.k_max, a.cand_mult, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                     a.cand_chunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool listed = SK && a.sketch_full;
+  if (listed && a.cand_mult == 1 && !a.fused)  // the selection is the sketch's own top-k
+    return launch_full_select_t<D, PAGED, true>(a, 1, a.k_max, a.indices, stream);
+  if (listed) {
+    if ((e = launch_full_select_t<D, PAGED, true>(a, a.cand_mult, a.list_stride, a.list_pos, stream)) != hipSuccess)
+      return e;
+  } else {
+    hipLaunchKernelGGL((sample_keys_kernel<D, PAGED, SK>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
+                       0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.sample_keys);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
+    const int rows_tile = a.GT < 16 ? a.GT : 16;
+    auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK>
+                               : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK> : score_cand_kernel<D, PAGED, 4, SK>);
+    hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
+                       page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req,
+                       a.k_max, a.cand_mult, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
+                       a.cand_chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
   // the largest list (at most 12288)
   const int64_t keep_max = SK ? (int64_t)a.list_stride : (int64_t)a.k_max;
@@ -1549,7 +1618,7 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G,
                        a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
                        a.cand_chunks, a.k_max, a.cand_mult, lds_cap, a.list_pos, a.list_score,
-                       a.list_stride, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
+                       a.list_stride, listed, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
   } else {
     auto sel = a.fused ? cand_select_kernel<D, PAGED, true> : cand_select_kernel<D, PAGED, false>;
     if (lds > 65536) {
@@ -1573,23 +1642,11 @@ static hipError_t launch_filtered(const TopkLaunch& a, hipStream_t stream) {
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   if (a.sketch) return launch_filtered<true>(a, stream);
   if (a.filtered) return launch_filtered<false>(a, stream);
-  hipError_t e = launch_fill_u32(a.hist, (int64_t)a.rows * kHistBins, 0u, stream);
-  if (e != hipSuccess) return e;
   if (a.D == 128)
-    e = a.paged ? launch_score_t<128, true>(a, stream) : launch_score_t<128, false>(a, stream);
-  else
-    e = a.paged ? launch_score_t<64, true>(a, stream) : launch_score_t<64, false>(a, stream);
-  if (e != hipSuccess) return e;
-  const size_t lds = select_lds_bytes(a.kv.max_len);
-  if (lds > 65536) {
-    e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const int words = ((a.kv.max_len + 255) / 256) * 8;
-  hipLaunchKernelGGL(select_kernel, dim3(a.rows), dim3(kSelThreads), lds, stream, a.scores,
-                     a.hist, a.kv.seq_lens, a.k_per_req, a.T, a.Hq, a.kv.max_len, a.score_stride,
-                     a.k_max, words, a.indices);
-  return hipGetLastError();
+    return a.paged ? launch_full_select_t<128, true, false>(a, 1, a.k_max, a.indices, stream)
+                   : launch_full_select_t<128, false, false>(a, 1, a.k_max, a.indices, stream);
+  return a.paged ? launch_full_select_t<64, true, false>(a, 1, a.k_max, a.indices, stream)
+                 : launch_full_select_t<64, false, false>(a, 1, a.k_max, a.indices, stream);
 }
 
 }  // namespace cs

@@ -10,8 +10,9 @@ against the CPU oracle in oracle/sketch.py.
   the fused step     index lists as above; (out, lse) against the oracle's sparse attention over
                      the list the step used, 2e-3 / 1e-3.
 Paths covered: candidates from the sampled threshold, the full-row fallback (planted keys at the
-sampled positions; and lists too long for the candidate slots), every visible position a
-candidate (cand_mult * k >= visible), k = 0 and k >= visible per request, paged and causal.
+sampled positions), lists longer than 1/16 of the cache (every sketch score, then select), every
+visible position a candidate (cand_mult * k >= visible), k = 0 and k >= visible per request,
+paged and causal.
 """
 
 import numpy as np
@@ -168,11 +169,12 @@ def test_sketch_indexer_all_positions_candidates_is_exact():
         check_topk_row(idx[b, t, hq], q[b, t, hq], oc.keys(b, hq // 2), vis, 400)
 
 
-def test_sketch_indexer_long_lists_fall_back():
-    # 2 * k = 1200 of 4096: more candidates than the slots hold, rows rescored in full
+@pytest.mark.parametrize("m", [1, 2])
+def test_sketch_indexer_long_lists_full_score_path(m):
+    # m * k >= 600 of 4096 (more than 1/16 of the cache): lists from every sketch score
     wl = make_workload(batch=2, q_len=1, num_q_heads=4, num_kv_heads=2, head_dim=128,
                        seq_lens=[4096, 3000], k=600, max_len=4096, seed=67)
-    _run(wl, m=2)
+    _run(wl, m=m)
 
 
 def test_sketch_indexer_unrepresentative_sample_falls_back():
