@@ -75,7 +75,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--sweep-k", default=None, help="k for a sweep workload (s10/s50/s100/s500/s1000)")
+    p.add_argument("--sweep-k", default=None, help="k for a sweep workload (s2/s5/s10/s20/s50/s100/s500/s1000)")
     p.add_argument("--cand-mult", type=int, default=2,
                    help="candidates per selected position of the reduced-byte indexer")
     p.add_argument("--sparse-splits", type=int, default=0)

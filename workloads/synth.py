@@ -291,7 +291,7 @@ NAMED = {
         k=2621, structure="lowrank", needles_per_head=0, seed=1003,
     ),
     # Sparsity sweep at fixed shape: 16 requests, GQA 32/8, d=128, N=131072; k is one of
-    # N/10, N/50, N/100, N/500, N/1000 (default N/50).
+    # N/2, N/5, N/10, N/20, N/50, N/100, N/500, N/1000 (default N/50).
     "sweep_b16_n128k": dict(
         batch=16, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=[131072] * 16,
         k=2621, structure="plain", needles_per_head=0, seed=1004,
@@ -311,7 +311,8 @@ NAMED = {
     ),
 }
 
-SWEEP_K = {"s10": 13107, "s50": 2621, "s100": 1310, "s500": 262, "s1000": 131}
+SWEEP_K = {"s2": 65536, "s5": 26214, "s10": 13107, "s20": 6553, "s50": 2621, "s100": 1310, "s500": 262,
+           "s1000": 131}
 
 
 def make_named(name: str, device="cpu", **overrides) -> Workload:
