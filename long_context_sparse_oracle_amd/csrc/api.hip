@@ -168,7 +168,7 @@ cs_status check_sketch(const cs_key_sketch* sk) {
 // keys, slot counts, the query rows' codes and scales, the candidate lists (positions, scores),
 // then the selected lists of the step.
 struct SketchWs {
-  size_t scores, hist, keys, counts, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
+  size_t scores, hist, keys, counts, tau, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
 };
 
 // Lists longer than 1/16 of the cache come from every sketch score (the candidate slots hold
@@ -188,7 +188,8 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
   w.keys = w.hist + (sketch_full(kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
   w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
-  w.q_codes = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  w.q_codes = w.tau + align_up(rows * sizeof(float));
   w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
   w.list_pos = w.q_scales + align_up(rows * sizeof(float));
   w.list_score = w.list_pos + align_up(rows * ls * sizeof(int32_t));
@@ -199,7 +200,7 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
 }
 
 struct TopkWs {
-  size_t scores, hist, keys, counts, total;
+  size_t scores, hist, keys, counts, tau, total;
 };
 
 TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
@@ -211,7 +212,8 @@ TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
   w.keys = w.hist + align_up(rows * 4096 * sizeof(uint32_t));
   w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
-  w.total = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
+  w.total = w.tau + align_up(rows * sizeof(float));
   return w;
 }
 
@@ -344,6 +346,7 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  a.tau = reinterpret_cast<float*>(ws + lay.tau);
   a.indices = indices;
   return a;
 }
@@ -542,6 +545,7 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  a.tau = reinterpret_cast<float*>(ws + lay.tau);
   a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);
   a.list_score = reinterpret_cast<float*>(ws + lay.list_score);
   a.list_stride = (int)sketch_list_stride(kv, k_max, cand_mult);

@@ -39,6 +39,7 @@ struct TopkLaunch {
   bool filtered;
   uint32_t* sample_keys;  // [rows, 1024]: ordered keys of the sampled scores
   uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
+  float* tau;         // [rows]: candidate thresholds
   // fused decode step (filtered path): selection and attention per row in one kernel
   bool fused;
   int32_t* sel_pos;   // [rows, k_max]

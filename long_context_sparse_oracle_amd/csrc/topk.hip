@@ -702,6 +702,26 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
   return key_to_float(P << 16);
 }
 
+// tau of every row (one wave per row) for score_cand_kernel; SK: for the row's
+// min(cand_mult * k', visible) largest sketch scores.
+template <bool SK>
+__global__ __launch_bounds__(4 * kWave) void tau_kernel(KVArgs kv, int T, int Hq, const int32_t* __restrict__ k_per_req,
+                                                       int k_max, int cand_mult, const uint32_t* __restrict__ sample_keys,
+                                                       float* __restrict__ tau, int rows) {
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  const int L = seq_len_of(kv, b);
+  const int vis = L - T + t + 1;
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, max(vis, 0));
+  const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
+  const float th = row_tau(sample_keys + (int64_t)row * kTauSamples, vis, keep, tau_stride(L));
+  if ((threadIdx.x & 63) == 0) tau[row] = th;
+}
+
 // Row mapping of the candidate pass: query row r of a 16-row tile sits in MFMA row
 // 4 * (r % 4) + r / 4, so lane group g4 (lanes 16 g4 .. 16 g4 + 15) holds rows 4 i + g4 for
 // i = 0..3 and, with 4 or 8 query rows, every lane group holds valid rows for the same i.
@@ -711,12 +731,10 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
 template <int D, bool PAGED, int NI, bool SK>
 __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
-    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult,
-    const uint32_t* __restrict__ sample_keys, float* __restrict__ region, int64_t score_stride,
+    const float* __restrict__ tau, float* __restrict__ region, int64_t score_stride,
     uint32_t* __restrict__ counts, int chunk, int chunks) {
   extern __shared__ int lds_pages[];
   __shared__ uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
-  __shared__ float th_s[16];
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int UNR = SK ? 2 * kScoreUnroll : kScoreUnroll;  // tiles per step: the same bytes in flight
   const int c = blockIdx.x;
@@ -742,23 +760,6 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
   const int wbeg = start + wave * span;
   const int wend = min(wbeg + span, end);
 
-  // thresholds of the workgroup's rows, one wave per row
-  {
-    int kb = k_per_req ? k_per_req[b] : k_max;
-    kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
-    const int stride = tau_stride(L);
-    for (int rl = wave; rl < rows_here; rl += kCandWaves) {
-      const int r = r0 + rl;
-      const int t = r / G, gi = r - (r / G) * G;
-      const int vis = L - T + t + 1;
-      const int kk = min(kb, max(vis, 0));
-      const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
-      const float th = row_tau(sample_keys + (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples,
-                               vis, keep, stride);
-      if (lane == 0) th_s[rl] = th;
-    }
-  }
-
   uint4 a[KS];
   {
     const int rl = 4 * (m & 3) + (m >> 2);  // query row of MFMA row m
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
     }
   }
-  __syncthreads();  // page ids and thresholds
+  __syncthreads();  // page ids
   // Candidate lines are written with buffer stores through one resource spanning this
   // workgroup's rows; a lane with nothing to write passes an offset past the resource, which
   // the hardware drops.  Every tile thus issues the same stores with no branch around them, and
@@ -785,8 +786,15 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     row_lo = ((int64_t)b * T + t0) * Hq + (h * G + r0 - t0 * G);
     row_hi = ((int64_t)b * T + t1) * Hq + (h * G + (r0 + rows_here - 1) - t1 * G);
   }
-  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      region + row_lo * score_stride, (short)0, (int)((row_hi - row_lo + 1) * score_stride * 4), 0x00020000);
+  // (base and size pass through readfirstlane: they are workgroup-uniform, and the compiler
+  // otherwise may keep the descriptor in vector registers and wrap every store in a loop over
+  // its distinct values)
+  const uint64_t out_addr = reinterpret_cast<uint64_t>(region + row_lo * score_stride);
+  const uint64_t out_base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(out_addr >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)out_addr);
+  const int out_bytes = __builtin_amdgcn_readfirstlane((int)((row_hi - row_lo + 1) * score_stride * 4));
+  const __amdgpu_buffer_rsrc_t out_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float*>(out_base), (short)0, out_bytes, 0x00020000);
   constexpr uint32_t kDrop = 0xfffffff0u;
   const uint32_t line_stride = (uint32_t)chunks * kCandWaves * 128u;  // bytes from line l to l + 1 of a slot
   // rows 4 i + g4 (i < NI = ceil(rows / 4), fixed at compile time) of this lane: visibility,
@@ -807,7 +815,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       const int t = r / G, gi = r - (r / G) * G;
       grow[i] = ((int64_t)b * T + t) * Hq + (h * G + gi);
       vis[i] = L - T + t + 1;
-      th[i] = th_s[rl];
+      th[i] = tau[grow[i]];
       qsc[i] = SK ? sk.q_scales[grow[i]] : 0.f;
     } else {
       grow[i] = 0;
@@ -1593,14 +1601,16 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL((sample_keys_kernel<D, PAGED, SK>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
                        0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.sample_keys);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tau_kernel<SK>, dim3((a.rows + 3) / 4), dim3(4 * kWave), 0, stream, a.kv, a.T, a.Hq,
+                       a.k_per_req, a.k_max, a.cand_mult, a.sample_keys, a.tau, a.rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
     const int rows_tile = a.GT < 16 ? a.GT : 16;
     auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK>
                                : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK> : score_cand_kernel<D, PAGED, 4, SK>);
     hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
-                       page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req,
-                       a.k_max, a.cand_mult, a.sample_keys, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                       a.cand_chunks);
+                       page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.tau,
+                       a.scores, a.score_stride, a.counts, a.cand_chunk, a.cand_chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
