@@ -332,6 +332,7 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   a.GT = gt_of(shape);
   a.D = shape->head_dim;
   a.rows = (int)rows_of(shape);
+  a.cus = cu_count();
   a.paged = kv->layout == CS_KV_PAGED;
   a.scale = sm_scale;
   a.k_per_req = k_per_req;

@@ -26,6 +26,7 @@ struct TopkLaunch {
   const uint16_t* q;
   KVArgs kv;
   int B, T, Hq, G, GT, D, rows;
+  int cus;  // compute units of the device
   bool paged;
   float scale;
   const int32_t* k_per_req;

@@ -964,7 +964,10 @@ struct DenseSource {
   }
 };
 
-constexpr int kCsMaxBlocks = 3;  // candidate blocks of kCsThreads * kCsPer held with positions in registers
+// Candidate blocks of kCsThreads * kCsPer held in LDS with their positions in registers: MB =
+// kCsBlocks, or kCsBlocksBig for long lists (more registers, fewer workgroups per CU).
+constexpr int kCsBlocks = 3;
+constexpr int kCsBlocksBig = 6;
 
 // Finds the kk-th largest key of the list (kmin <= every key <= kmax) by radix select over the
 // bits below their common prefix, in digits of up to 11 bits; hist holds 2048 counters.
@@ -1167,7 +1170,9 @@ __device__ void attend_list(const KVArgs& kv, int b, int h, const int32_t* __res
   }
 }
 
-// The candidate part of cand_select_kernel: select from the row's slots.
+// The candidate part of cand_select_kernel: select from the row's slots (held in LDS when at most
+// lds_cap <= MB * kCsThreads * kCsPer of them).
+template <int MB>
 __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, int kk, int k_max,
                           int row, float* __restrict__ region, int64_t score_stride, int chunks,
                           const uint32_t* prefix_s, uint32_t* lds_key, int lds_cap, uint32_t* hist,
@@ -1191,10 +1196,10 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
     sh.kmax = 0u;
   }
   __syncthreads();
-  uint32_t preg[kCsMaxBlocks][kCsPer];
+  uint32_t preg[MB][kCsPer];
   uint32_t lmin = 0xffffffffu, lmax = 0u;
 #pragma unroll
-  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+  for (int blk = 0; blk < MB; ++blk) {
     const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
     if (blk * kCsThreads * kCsPer >= (int)total) break;
     int64_t off[kCsPer];
@@ -1222,7 +1227,7 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
   const bool take_all_eq = cnt_eq == need;
   uint32_t eq_base = 0, out_base = 0;
 #pragma unroll
-  for (int blk = 0; blk < kCsMaxBlocks; ++blk) {
+  for (int blk = 0; blk < MB; ++blk) {
     if (blk * kCsThreads * kCsPer >= (int)total) break;
     const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
     uint32_t keys[kCsPer];
@@ -1268,7 +1273,7 @@ __device__ uint32_t slot_prefix(const uint32_t* __restrict__ counts, int row, in
 // FUSED (the decode step): the selection also goes to the row's (position, score) list in
 // sel_pos / sel_score, the workgroup then attends to it (attend_list) and writes out / lse;
 // indices may then be nullptr.
-template <int D, bool PAGED, bool FUSED>
+template <int D, bool PAGED, bool FUSED, int MB>
 __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, int T, int Hq, int G, float scale,
     const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
@@ -1334,7 +1339,7 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     __syncthreads();
     select_ordered(DenseSource{srow}, vis, kk, k_max, so, hist, sh);
   } else {
-    cand_path(total, nsub, cap, so, kk, k_max, row, region, score_stride, chunks, prefix_s, lds_key,
+    cand_path<MB>(total, nsub, cap, so, kk, k_max, row, region, score_stride, chunks, prefix_s, lds_key,
               lds_cap, hist, sh);
   }
   if constexpr (FUSED) {
@@ -1441,7 +1446,7 @@ __device__ void rerank_exact(const KVArgs& kv, int b, int h, const uint16_t* __r
 // with `listed` the positions are already there (select_kernel over every sketch score).
 // FUSED: as for cand_select_kernel, the selection also goes to sel_pos / sel_score and the row's
 // attention over it to out / lse.
-template <int D, bool PAGED, bool FUSED>
+template <int D, bool PAGED, bool FUSED, int MB>
 __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
     const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
@@ -1504,7 +1509,7 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
       __syncthreads();
       select_ordered(DenseSource{srow}, vis, nc, lk, lo, hist, sh);
     } else {
-      cand_path(total, nsub, cap, lo, nc, lk, row, region, score_stride, chunks, prefix_s, lds_key,
+      cand_path<MB>(total, nsub, cap, lo, nc, lk, row, region, score_stride, chunks, prefix_s, lds_key,
                 lds_cap, hist, sh);
     }
     if (direct) return;
@@ -1614,13 +1619,17 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
-  // the largest list (at most 12288)
+  // the largest list, at most kCsBlocks * kCsThreads * kCsPer = 12288; when there are no more rows
+  // than compute units (one workgroup per unit anyway), up to twice that
   const int64_t keep_max = SK ? (int64_t)a.list_stride : (int64_t)a.k_max;
   int lds_cap = (int)((keep_max * 9 / 2 + 255) / 256 * 256);
-  if (lds_cap > kCsMaxBlocks * kCsThreads * kCsPer) lds_cap = kCsMaxBlocks * kCsThreads * kCsPer;
+  const bool big = lds_cap > kCsBlocks * kCsThreads * kCsPer && a.rows <= a.cus;
+  const int cap_max = (big ? kCsBlocksBig : kCsBlocks) * kCsThreads * kCsPer;
+  if (lds_cap > cap_max) lds_cap = cap_max;
   const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
   if constexpr (SK) {
-    auto sel = a.fused ? sketch_select_kernel<D, PAGED, true> : sketch_select_kernel<D, PAGED, false>;
+    auto sel = a.fused ? (big ? sketch_select_kernel<D, PAGED, true, kCsBlocksBig> : sketch_select_kernel<D, PAGED, true, kCsBlocks>)
+                       : (big ? sketch_select_kernel<D, PAGED, false, kCsBlocksBig> : sketch_select_kernel<D, PAGED, false, kCsBlocks>);
     if (lds > 65536) {
       e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
@@ -1630,7 +1639,8 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
                        a.cand_chunks, a.k_max, a.cand_mult, lds_cap, a.list_pos, a.list_score,
                        a.list_stride, listed, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
   } else {
-    auto sel = a.fused ? cand_select_kernel<D, PAGED, true> : cand_select_kernel<D, PAGED, false>;
+    auto sel = a.fused ? (big ? cand_select_kernel<D, PAGED, true, kCsBlocksBig> : cand_select_kernel<D, PAGED, true, kCsBlocks>)
+                       : (big ? cand_select_kernel<D, PAGED, false, kCsBlocksBig> : cand_select_kernel<D, PAGED, false, kCsBlocks>);
     if (lds > 65536) {
       e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;

@@ -88,3 +88,11 @@ def test_paged_filtered_causal():
                        seq_lens=[20000, 5000, 900], k=0.02, layout="paged", page_size=16,
                        max_len=20480, needles_per_head=2, seed=45)
     _check_indexer(wl)
+
+
+def test_filtered_long_lists_large_capacity_select():
+    # k = 3000 of 65536 on 8 rows: the candidate lists exceed 12288 keys, so the selection runs
+    # in the workgroup variant that holds up to 24576 of them in LDS
+    wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                       seq_lens=[65536], k=3000, seed=46)
+    _check_indexer(wl)

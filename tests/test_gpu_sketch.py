@@ -206,3 +206,10 @@ def test_sketch_llama3_8b_n32k_k655_sampled_rows():
     rng = np.random.default_rng(71)
     rows = [(0, 0, 0), (7, 0, 31)] + [(int(rng.integers(8)), 0, int(rng.integers(32))) for _ in range(4)]
     _run(wl, m=2, rows=rows, step=True)
+
+
+def test_sketch_long_lists_large_capacity_select():
+    # 2 * k = 3000 of 65536 on 8 rows: the selection variant holding up to 24576 candidates
+    wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                       seq_lens=[65536], k=1500, seed=72)
+    _run(wl, m=2, step=True)
