@@ -290,23 +290,8 @@ cs_status check_ws(void* ws, size_t bytes, size_t need) {
   return CS_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-const char* cs_status_str(cs_status s) {
-  switch (s) {
-    case CS_OK: return "CS_OK";
-    case CS_ERR_INVALID_ARG: return "CS_ERR_INVALID_ARG";
-    case CS_ERR_UNSUPPORTED: return "CS_ERR_UNSUPPORTED";
-    case CS_ERR_WORKSPACE_TOO_SMALL: return "CS_ERR_WORKSPACE_TOO_SMALL";
-    case CS_ERR_HIP: return "CS_ERR_HIP";
-  }
-  return "CS_ERR_UNKNOWN";
-}
-
-int32_t cs_version(void) { return 100; }
-
+// ---- launch descriptors
 cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
                            float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
                            void* workspace) {
@@ -352,31 +337,6 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   return a;
 }
 
-size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max) {
-  (void)k_max;
-  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK) return 0;
-  return topk_ws(shape, kv);
-}
-
-cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
-                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  cs_status st = check_shape(shape);
-  if (st != CS_OK) return st;
-  if ((st = check_kv(shape, kv)) != CS_OK) return st;
-  if (!q || !indices || !aligned(q, 16) || !aligned(indices, 4)) return CS_ERR_INVALID_ARG;
-  if (k_per_req && !aligned(k_per_req, 4)) return CS_ERR_INVALID_ARG;
-  if (k_max < 1 || k_max > kv->max_len) return CS_ERR_INVALID_ARG;
-  if (!std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
-  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
-  const size_t need = topk_ws(shape, kv);
-  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
-
-  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, workspace);
-  hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
-}
-
 cs::AttnLaunch sparse_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
                              const int32_t* indices, int32_t k_max, float sm_scale,
                              const SparsePlan& plan, float* out, float* lse, void* workspace) {
@@ -407,6 +367,105 @@ cs::AttnLaunch sparse_launch(const cs_decode_shape* shape, const void* q, const 
   return a;
 }
 
+// ---- fused decode step: indexer + sparse attention in one call
+// Workspace: the indexer's, then the selected lists (int32 positions and float32 scores,
+// [rows, k_max] each), then the sparse attention's partials on the full-score path.
+struct StepWs {
+  size_t topk, sel_pos, sel_score, attn, total;
+};
+
+StepWs step_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max) {
+  const size_t rows = (size_t)rows_of(s);
+  StepWs w;
+  w.topk = 0;
+  w.sel_pos = align_up(topk_ws(s, kv));
+  w.sel_score = w.sel_pos + align_up(rows * (size_t)k_max * sizeof(int32_t));
+  w.attn = w.sel_score + align_up(rows * (size_t)k_max * sizeof(float));
+  w.total = w.attn + attn_ws(s, sparse_plan(s, k_max, 0).S);
+  return w;
+}
+
+cs_status check_sketch_call(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                            const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                            int32_t k_max, int32_t cand_mult, const int32_t* indices) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if ((st = check_sketch(sketch)) != CS_OK) return st;
+  if (!q || !aligned(q, 16)) return CS_ERR_INVALID_ARG;
+  if ((indices && !aligned(indices, 4)) || (k_per_req && !aligned(k_per_req, 4))) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (cand_mult < 1 || cand_mult > kMaxCandMult) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen || !sketch_supported(shape, kv)) return CS_ERR_UNSUPPORTED;
+  return CS_OK;
+}
+
+cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                             const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
+                             int32_t k_max, int32_t cand_mult, int32_t* indices, char* ws,
+                             const SketchWs& lay) {
+  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws);
+  a.filtered = true;
+  a.sketch = true;
+  a.cand_mult = cand_mult;
+  a.sk.codes = static_cast<const int8_t*>(sketch->codes);
+  a.sk.scales = sketch->scales;
+  a.sk.q_codes = reinterpret_cast<int8_t*>(ws + lay.q_codes);
+  a.sk.q_scales = reinterpret_cast<float*>(ws + lay.q_scales);
+  a.scores = reinterpret_cast<float*>(ws + lay.scores);
+  a.sketch_full = sketch_full(kv, k_max, cand_mult);
+  a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
+  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
+  a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
+  a.tau = reinterpret_cast<float*>(ws + lay.tau);
+  a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);
+  a.list_score = reinterpret_cast<float*>(ws + lay.list_score);
+  a.list_stride = (int)sketch_list_stride(kv, k_max, cand_mult);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cs_status_str(cs_status s) {
+  switch (s) {
+    case CS_OK: return "CS_OK";
+    case CS_ERR_INVALID_ARG: return "CS_ERR_INVALID_ARG";
+    case CS_ERR_UNSUPPORTED: return "CS_ERR_UNSUPPORTED";
+    case CS_ERR_WORKSPACE_TOO_SMALL: return "CS_ERR_WORKSPACE_TOO_SMALL";
+    case CS_ERR_HIP: return "CS_ERR_HIP";
+  }
+  return "CS_ERR_UNKNOWN";
+}
+
+int32_t cs_version(void) { return 100; }
+
+size_t topk_index_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max) {
+  (void)k_max;
+  if (check_shape(shape) != CS_OK || check_kv(shape, kv) != CS_OK) return 0;
+  return topk_ws(shape, kv);
+}
+
+cs_status topk_index(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                     float sm_scale, const int32_t* k_per_req, int32_t k_max, int32_t* indices,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !indices || !aligned(q, 16) || !aligned(indices, 4)) return CS_ERR_INVALID_ARG;
+  if (k_per_req && !aligned(k_per_req, 4)) return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || k_max > kv->max_len) return CS_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  if (kv->max_len > kTopkMaxLen) return CS_ERR_UNSUPPORTED;
+  const size_t need = topk_ws(shape, kv);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
+
+  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, workspace);
+  hipError_t e = cs::launch_topk(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
 size_t sparse_decode_attn_workspace_size(const cs_decode_shape* shape, int32_t k_max,
                                          int32_t num_splits) {
   if (check_shape(shape) != CS_OK || k_max < 1 || num_splits < 0) return 0;
@@ -432,24 +491,6 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   cs::AttnLaunch a = sparse_launch(shape, q, kv, indices, k_max, sm_scale, plan, out, lse, workspace);
   hipError_t e = cs::launch_sparse(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
-}
-
-// ---- fused decode step: indexer + sparse attention in one call
-// Workspace: the indexer's, then the selected lists (int32 positions and float32 scores,
-// [rows, k_max] each), then the sparse attention's partials on the full-score path.
-struct StepWs {
-  size_t topk, sel_pos, sel_score, attn, total;
-};
-
-StepWs step_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max) {
-  const size_t rows = (size_t)rows_of(s);
-  StepWs w;
-  w.topk = 0;
-  w.sel_pos = align_up(topk_ws(s, kv));
-  w.sel_score = w.sel_pos + align_up(rows * (size_t)k_max * sizeof(int32_t));
-  w.attn = w.sel_score + align_up(rows * (size_t)k_max * sizeof(float));
-  w.total = w.attn + attn_ws(s, sparse_plan(s, k_max, 0).S);
-  return w;
 }
 
 size_t sparse_decode_step_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv,
@@ -511,49 +552,6 @@ cs_status key_sketch_build(const cs_decode_shape* shape, const cs_kv_desc* kv, i
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
 }
-
-namespace {
-
-cs_status check_sketch_call(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
-                            const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
-                            int32_t k_max, int32_t cand_mult, const int32_t* indices) {
-  cs_status st = check_shape(shape);
-  if (st != CS_OK) return st;
-  if ((st = check_kv(shape, kv)) != CS_OK) return st;
-  if ((st = check_sketch(sketch)) != CS_OK) return st;
-  if (!q || !aligned(q, 16)) return CS_ERR_INVALID_ARG;
-  if ((indices && !aligned(indices, 4)) || (k_per_req && !aligned(k_per_req, 4))) return CS_ERR_INVALID_ARG;
-  if (k_max < 1 || k_max > kv->max_len || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
-  if (cand_mult < 1 || cand_mult > kMaxCandMult) return CS_ERR_INVALID_ARG;
-  if (kv->max_len > kTopkMaxLen || !sketch_supported(shape, kv)) return CS_ERR_UNSUPPORTED;
-  return CS_OK;
-}
-
-cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
-                             const cs_key_sketch* sketch, float sm_scale, const int32_t* k_per_req,
-                             int32_t k_max, int32_t cand_mult, int32_t* indices, char* ws,
-                             const SketchWs& lay) {
-  cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws);
-  a.filtered = true;
-  a.sketch = true;
-  a.cand_mult = cand_mult;
-  a.sk.codes = static_cast<const int8_t*>(sketch->codes);
-  a.sk.scales = sketch->scales;
-  a.sk.q_codes = reinterpret_cast<int8_t*>(ws + lay.q_codes);
-  a.sk.q_scales = reinterpret_cast<float*>(ws + lay.q_scales);
-  a.scores = reinterpret_cast<float*>(ws + lay.scores);
-  a.sketch_full = sketch_full(kv, k_max, cand_mult);
-  a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
-  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
-  a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
-  a.tau = reinterpret_cast<float*>(ws + lay.tau);
-  a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);
-  a.list_score = reinterpret_cast<float*>(ws + lay.list_score);
-  a.list_stride = (int)sketch_list_stride(kv, k_max, cand_mult);
-  return a;
-}
-
-}  // namespace
 
 size_t topk_index_sketch_workspace_size(const cs_decode_shape* shape, const cs_kv_desc* kv, int32_t k_max,
                                         int32_t cand_mult) {

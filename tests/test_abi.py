@@ -31,7 +31,9 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("topk_index", "sparse_decode_attn", "dense_decode_attn", "topk_index_workspace_size",
               "sparse_decode_attn_workspace_size", "dense_decode_attn_workspace_size",
-              "sparse_decode_step", "sparse_decode_step_workspace_size", "cs_status_str", "cs_version"):
+              "sparse_decode_step", "sparse_decode_step_workspace_size", "key_sketch_build",
+              "topk_index_sketch", "topk_index_sketch_workspace_size", "sparse_decode_step_sketch",
+              "sparse_decode_step_sketch_workspace_size", "cs_status_str", "cs_version"):
         assert n in names
 
 
@@ -42,6 +44,9 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     missing = [n for n in declared if n not in exported]
     assert not missing, missing
+    # no undeclared C-linkage function leaks out of the library (C++ symbols are mangled "_Z...")
+    extra = sorted(n for n in exported if not n.startswith("_Z") and n not in declared)
+    assert not extra, extra
     from long_context_sparse_oracle_amd import _lib
 
     assert sorted(_lib.EXPORTS) == declared
@@ -222,3 +227,54 @@ def test_workspace_sizes(lib):
     assert d(1) == 0 and 0 < d(2) < d(8)
     # invalid inputs give 0
     assert L.sparse_decode_attn_workspace_size(ctypes.byref(_shape(d=96)), 100, 2) == 0
+
+
+def _sketch_desc(codes=FAKE, scales=FAKE):
+    from long_context_sparse_oracle_amd._lib import KeySketchDesc
+
+    return KeySketchDesc(codes, scales)
+
+
+def _sketch_topk(L, shape, kv, sk, k_max=10, m=2, scale=0.088, ws=FAKE, ws_bytes=1 << 40, q=FAKE, idx=FAKE):
+    skp = ctypes.byref(sk) if sk is not None else None
+    return L.topk_index_sketch(ctypes.byref(shape), q, ctypes.byref(kv), skp, scale, None, k_max, m, idx, ws,
+                               ws_bytes, None)
+
+
+def _sketch_step(L, shape, kv, sk, k_max=10, m=2, ws=FAKE, ws_bytes=1 << 40, out=FAKE, lse=FAKE):
+    return L.sparse_decode_step_sketch(ctypes.byref(shape), FAKE, ctypes.byref(kv), ctypes.byref(sk), 0.088,
+                                       None, k_max, m, None, out, lse, ws, ws_bytes, None)
+
+
+def test_sketch_arguments(lib):
+    L = lib.LIB
+    sk = _sketch_desc()
+    # the sketch itself
+    assert L.key_sketch_build(ctypes.byref(_shape()), ctypes.byref(_kv()), 0, None, None) == INVALID
+    assert L.key_sketch_build(ctypes.byref(_shape()), ctypes.byref(_kv()), 0,
+                              ctypes.byref(_sketch_desc(codes=0)), None) == INVALID
+    assert L.key_sketch_build(ctypes.byref(_shape()), ctypes.byref(_kv()), 0,
+                              ctypes.byref(_sketch_desc(codes=FAKE + 8)), None) == INVALID
+    assert L.key_sketch_build(ctypes.byref(_shape()), ctypes.byref(_kv()), 0,
+                              ctypes.byref(_sketch_desc(scales=FAKE + 2)), None) == INVALID
+    assert L.key_sketch_build(ctypes.byref(_shape()), ctypes.byref(_kv()), -1, ctypes.byref(sk), None) == INVALID
+    assert L.key_sketch_build(ctypes.byref(_shape(d=96)), ctypes.byref(_kv()), 0, ctypes.byref(sk), None) == UNSUPPORTED
+    # the indexer and the step
+    assert _sketch_topk(L, _shape(), _kv(), None) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(), sk, m=0) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(), sk, m=65) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(), sk, k_max=0) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(), sk, idx=0) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(), sk, scale=float("nan")) == INVALID
+    assert _sketch_topk(L, _shape(), _kv(max_len=262145), sk) == UNSUPPORTED
+    assert _sketch_step(L, _shape(), _kv(), sk, out=0) == INVALID
+    assert _sketch_step(L, _shape(), _kv(), sk, m=0) == INVALID
+    need = L.topk_index_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 2)
+    assert need > 0
+    assert _sketch_topk(L, _shape(), _kv(), sk, ws_bytes=need - 1) == WS_SMALL
+    need_s = L.sparse_decode_step_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 2)
+    assert need_s > need
+    assert _sketch_step(L, _shape(), _kv(), sk, ws_bytes=need_s - 1) == WS_SMALL
+    # more candidates need more list room
+    assert need < L.topk_index_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 8)
+    assert L.topk_index_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 0) == 0
