@@ -6,6 +6,9 @@ log-sum-exp, and a 1e-3 band around the k-th score for selected sets):
              oracle's k-th largest score; the GPU row holds exactly min(k_b, visible) distinct
              visible positions in ascending order, then -1.
   attention  max |out - out_oracle| <= 2e-3 and |lse - lse_oracle| <= 1e-3 per row.
+  sketch     (reduced-byte indexer) every selected position lies in the oracle's candidate set,
+             which the GPU reproduces exactly, and the selection differs from the oracle's only at
+             positions within 1e-3 of the k-th largest exact score among the candidates.
 """
 
 import math
@@ -57,6 +60,29 @@ def check_topk_row(gpu_row, q_row, K, vis, k, where=""):
     if diff.size:
         s = oracle.scaled_scores(q_row, K[:vis])
         sk = float(np.sort(s)[::-1][kk - 1])
+        bad = diff[np.abs(s[diff] - sk) > BAND]
+        assert bad.size == 0, f"{where}: {bad.size} positions outside the band, e.g. {bad[:5]}"
+    return int(diff.size)
+
+
+def check_sketch_row(gpu_row, q_row, K, vis, k, m, where=""):
+    """Comparison of one GPU row of the reduced-byte indexer (cand_mult m) with its oracle."""
+    kk = min(k, vis)
+    row = np.asarray(gpu_row)
+    sel = row[:kk]
+    assert (row[kk:] == -1).all(), f"{where}: padding"
+    assert (sel >= 0).all() and (sel < vis).all(), f"{where}: out of range"
+    assert (np.diff(sel) > 0).all(), f"{where}: not strictly ascending"
+    if kk == 0:
+        return 0
+    cand = oracle.sketch_candidates(q_row, K, vis, kk, m)
+    outside = np.setdiff1d(sel, cand)
+    assert outside.size == 0, f"{where}: {outside.size} positions outside the sketch candidates, e.g. {outside[:5]}"
+    want = oracle.row_topk_sketch(q_row, K, vis, kk, m)
+    diff = np.setxor1d(sel, want)
+    if diff.size:
+        s = oracle.scaled_scores(q_row, K[:vis])
+        sk = float(np.sort(s[cand])[::-1][kk - 1])
         bad = diff[np.abs(s[diff] - sk) > BAND]
         assert bad.size == 0, f"{where}: {bad.size} positions outside the band, e.g. {bad[:5]}"
     return int(diff.size)

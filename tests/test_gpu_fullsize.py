@@ -2,7 +2,9 @@
 (automatic splits and chunking), including the sweep's 500x point and its 64-request batch.
 
 * Sampled rows (first, last and seeded random ones) are compared with the CPU oracle one by one:
-  indexer by the band rule, sparse attention fed the oracle's own index lists, dense attention.
+  indexer by the band rule, sparse attention fed the oracle's own index lists, dense attention;
+  the one-call step and the reduced-byte indexer's step (cand_mult 2, as bench.py runs them):
+  their lists by the band rules, their outputs against the oracle's attention over those lists.
 * Every row is checked for properties that hold at any size: each index row holds min(k_b,
   visible) distinct visible positions in ascending order then -1; every planted needle is
   selected; and against float32 scores computed independently with torch on the GPU, every
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 from tests._util import bits
-from tests.gpu_util import check_attn_row, check_topk_row, logical_kv
+from tests.gpu_util import check_attn_row, check_sketch_row, check_topk_row, logical_kv
 from workloads import make_named, random_index_sets
 from workloads.synth import SWEEP_K
 
@@ -91,6 +93,48 @@ def _check_all_rows(wl, idx, kreq):
         assert p in idx[b, t, hq].tolist(), f"needle {(b, t, hq, p)} not selected"
 
 
+def _check_structure(wl, idx, kreq):
+    """Padding, range and order of every row of an index tensor."""
+    B, T = wl.batch, wl.q_len
+    for b in range(B):
+        L = int(wl.seq_lens[b])
+        for t in range(T):
+            vis = L - T + t + 1
+            kk = min(int(kreq[b]), vis)
+            rows = idx[b, t]
+            sel = rows[:, :kk].long()
+            assert bool((rows[:, kk:] == -1).all()), f"padding b{b} t{t}"
+            assert bool(((sel >= 0) & (sel < vis)).all()), f"range b{b} t{t}"
+            if kk > 1:
+                assert bool((sel[:, 1:] > sel[:, :-1]).all()), f"ascending b{b} t{t}"
+
+
+def _check_steps(wl, cache, kt, k_max, kreq, rows, q):
+    """The one-call step and the reduced-byte indexer's step at full size, on sampled rows."""
+    m = _lib()
+    o, l, idx = m.sparse_decode_step(wl.q, cache, kt, k_max=k_max, return_indices=True)
+    sketch = m.key_sketch_build(cache)
+    o2, l2, idx2 = m.sparse_decode_step_sketch(wl.q, cache, sketch, kt, k_max=k_max, cand_mult=2,
+                                               return_indices=True)
+    torch.cuda.synchronize()
+    _check_structure(wl, idx, kreq)
+    _check_structure(wl, idx2, kreq)
+    o, l, idx = o.cpu().numpy(), l.cpu().numpy(), idx.cpu().numpy()
+    o2, l2, idx2 = o2.cpu().numpy(), l2.cpu().numpy(), idx2.cpu().numpy()
+    del sketch
+    G = wl.group
+    for b, t, hq in rows:
+        K, V = logical_kv(wl, b, hq // G)
+        vis = oracle.visible_length(int(wl.seq_lens[b]), wl.q_len, t)
+        kk = int(kreq[b])
+        check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, kk, f"step topk {(b, t, hq)}")
+        want = oracle.row_sparse(q[b, t, hq], K, V, idx[b, t, hq], vis)
+        check_attn_row(o[b, t, hq], l[b, t, hq], want[0], want[1], f"step {(b, t, hq)}")
+        check_sketch_row(idx2[b, t, hq], q[b, t, hq], K, vis, kk, 2, f"sketch topk {(b, t, hq)}")
+        want = oracle.row_sparse(q[b, t, hq], K, V, idx2[b, t, hq], vis)
+        check_attn_row(o2[b, t, hq], l2[b, t, hq], want[0], want[1], f"sketch step {(b, t, hq)}")
+
+
 def _run(wl, k=None, seed=0, check_dense=True):
     m = _lib()
     cache = _cache(wl)
@@ -141,6 +185,7 @@ def _run(wl, k=None, seed=0, check_dense=True):
         for r, (_, dn) in ref.items():
             if dn is not None:
                 check_attn_row(od[r], ld[r], dn[0], dn[1], f"dense {r}")
+    _check_steps(wl, cache, kt, k_max, kreq, rows, q)
 
 
 def test_llama3_8b_n32k_k655():
@@ -161,7 +206,7 @@ def sweep_wl():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("level", ["s10", "s50", "s100", "s500", "s1000"])
+@pytest.mark.parametrize("level", ["s2", "s5", "s10", "s20", "s50", "s100", "s500", "s1000"])
 def test_sweep_b16_n128k(sweep_wl, level):
     _run(sweep_wl, k=SWEEP_K[level], seed=13, check_dense=(level == "s50"))
 

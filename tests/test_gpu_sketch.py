@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from tests._util import bits, oracle_cache
-from tests.gpu_util import BAND, all_rows, cache_of, check_attn_row, logical_kv
+from tests.gpu_util import all_rows, cache_of, check_attn_row, check_sketch_row, logical_kv
 from workloads import make_named, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -31,28 +31,6 @@ def _lib():
     import long_context_sparse_oracle_amd as m
 
     return m
-
-
-def check_sketch_row(gpu_row, q_row, K, vis, k, m, where=""):
-    kk = min(k, vis)
-    row = np.asarray(gpu_row)
-    sel = row[:kk]
-    assert (row[kk:] == -1).all(), f"{where}: padding"
-    assert (sel >= 0).all() and (sel < vis).all(), f"{where}: out of range"
-    assert (np.diff(sel) > 0).all(), f"{where}: not strictly ascending"
-    if kk == 0:
-        return 0
-    cand = oracle.sketch_candidates(q_row, K, vis, kk, m)
-    outside = np.setdiff1d(sel, cand)
-    assert outside.size == 0, f"{where}: {outside.size} positions outside the sketch candidates, e.g. {outside[:5]}"
-    want = oracle.row_topk_sketch(q_row, K, vis, kk, m)
-    diff = np.setxor1d(sel, want)
-    if diff.size:
-        s = oracle.scaled_scores(q_row, K[:vis])
-        sk = float(np.sort(s[cand])[::-1][kk - 1])
-        bad = diff[np.abs(s[diff] - sk) > BAND]
-        assert bad.size == 0, f"{where}: {bad.size} positions outside the band, e.g. {bad[:5]}"
-    return int(diff.size)
 
 
 def _run(wl_cpu, m, k_max=None, rows=None, step=False):
