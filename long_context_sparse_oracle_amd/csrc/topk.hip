@@ -554,8 +554,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // suggest (the writes interleave with the K stream), so for k <= N/16 the indexer avoids them:
 //  A. sample_keys_kernel scores a strided sample of at most kTauSamples positions per (request,
 //     KV head) and stores the ordered keys of each row's samples;
-//  B. score_cand_kernel first sets, per row, a threshold tau: the 16-bit key prefix of the
-//     sample's r-th largest score, r ~ kCandFactor * k * (samples / visible).  It then scores
+//  B. tau_kernel sets, per row, a threshold tau: the 16-bit key prefix of the sample's r-th
+//     largest score, r ~ kCandFactor * k * (samples / visible).  score_cand_kernel then scores
 //     every position once, as score_hist_kernel does, and keeps only the candidates s >= tau as
 //     (position, score) pairs, staged in LDS and written a 128-byte line at a time into per-wave
 //     slots of the workspace.  A wave scans one contiguous range, so the slots concatenated in
