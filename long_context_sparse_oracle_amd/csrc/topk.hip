@@ -11,6 +11,7 @@
 namespace cs {
 
 typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 constexpr int kHistBins = 4096;      // 12 leading bits of the ordered key
 constexpr int kScoreMaxThreads = 1024;  // up to 16 waves (4 per 4 query rows of the group)
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     const float* __restrict__ tau, float* __restrict__ region, int64_t score_stride,
     uint32_t* __restrict__ counts, int chunk, int chunks) {
   extern __shared__ int lds_pages[];
-  __shared__ uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
+  __shared__ __align__(16) uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int UNR = kScoreUnroll;  // tiles per step (twice as many for the sketch measured no faster)
   const int c = blockIdx.x;
@@ -867,12 +868,36 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
         if (pred) st[(head[i] + fill[i] + __popc(seg & ((1u << m) - 1u))) & 31u] =
             make_uint2((uint32_t)n, __float_as_uint(s));
         fill[i] += __popc(seg);
+        if constexpr (NI == 1) {
+          wave_lds_fence();
+          const uint2 v = st[(head[i] + m) & 31u];
+          const bool full = fill[i] >= 16u;
+          const bool write = full && valid[i] && done[i] + 16u <= (uint32_t)cap;
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
+                                                (int)(write ? slot[i] + (done[i] / 16u) * line_stride + m * 8u : kDrop), 0, 0);
+        }
+      }
+      if constexpr (NI >= 2) {
+        // rows 4 i + g4 and 4 (i + 1) + g4 share one 16-byte store per lane: lanes 8 h .. 8 h + 7
+        // of lane group g4 write the line of row 4 (i + h) + g4, two pairs each
         wave_lds_fence();
-        const uint2 v = st[(head[i] + m) & 31u];
+        const uint32_t h = (uint32_t)(m >> 3) & 1u, j = (uint32_t)m & 7u;
+#pragma unroll
+        for (int i = 0; i < NI; i += 2) {
+          const uint32_t hd = h ? head[i + 1] : head[i];
+          const uint32_t fl = h ? fill[i + 1] : fill[i];
+          const uint32_t dn = h ? done[i + 1] : done[i];
+          const uint32_t sl = h ? slot[i + 1] : slot[i];
+          const bool vd = h ? valid[i + 1] : valid[i];
+          const uint4 v = *reinterpret_cast<const uint4*>(&stage[wave][4 * (i + (int)h) + g4][(hd + 2u * j) & 31u]);
+          const bool write = fl >= 16u && vd && dn + 16u <= (uint32_t)cap;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), out_rsrc,
+                                                 (int)(write ? sl + (dn / 16u) * line_stride + j * 16u : kDrop), 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
         const bool full = fill[i] >= 16u;
-        const bool write = full && valid[i] && done[i] + 16u <= (uint32_t)cap;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
-                                              (int)(write ? slot[i] + (done[i] / 16u) * line_stride + m * 8u : kDrop), 0, 0);
         head[i] = full ? (head[i] + 16u) & 31u : head[i];
         done[i] += full ? 16u : 0u;
         fill[i] -= full ? 16u : 0u;
