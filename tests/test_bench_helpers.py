@@ -1,0 +1,46 @@
+"""CPU checks of bench.py's accounting: algorithmic bytes, re-rank row counts and recall."""
+
+import torch
+
+import bench
+from workloads import make_workload
+
+
+def _wl():
+    return make_workload(batch=2, q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                         seq_lens=[100, 10], k=[8, 20], max_len=128, seed=3)
+
+
+def test_rerank_rows_counts_min_of_mk_and_visible():
+    wl = _wl()
+    # request 0: k' = 8 for both tokens (visible 99, 100); request 1: k' = min(20, 9) = 9, then 10
+    want_m2 = 4 * (min(16, 99) + min(16, 100)) + 4 * (min(18, 9) + min(20, 10))
+    assert bench.rerank_rows(wl, 2) == want_m2
+    want_m1 = 4 * (8 + 8) + 4 * (9 + 10)
+    assert bench.rerank_rows(wl, 1) == want_m1
+
+
+def test_recall():
+    a = torch.tensor([[[[0, 1, 2, -1]]]], dtype=torch.int32)
+    b = torch.tensor([[[[1, 2, 3, -1]]]], dtype=torch.int32)
+    assert abs(bench.recall(a, b, 8) - 2 / 3) < 1e-12
+    assert bench.recall(b, b, 8) == 1.0
+    empty = torch.full((1, 1, 1, 4), -1, dtype=torch.int32)
+    assert bench.recall(a, empty, 8) == 1.0
+
+
+def test_algorithmic_bytes_distinct_rows():
+    wl = _wl()
+    B, T, Hq, d = 2, 2, 4, 64
+    # every query row selects positions 0..3: per (request, KV head) 4 distinct rows
+    idx = torch.full((B, T, Hq, 20), -1, dtype=torch.int32)
+    idx[..., :4] = torch.arange(4, dtype=torch.int32)
+    ab = bench.algorithmic_bytes(wl, idx, 2)
+    assert ab["distinct_rows"] == B * 2 * 4
+    assert ab["selected_rows"] == B * T * Hq * 4
+    rows = B * T * Hq
+    q_bytes, o_bytes = rows * d * 2, rows * d * 4 + rows * 4
+    assert ab["sparse"] == 2 * ab["distinct_rows"] * d * 2 + idx.numel() * 4 + q_bytes + o_bytes
+    tokens = 110
+    assert ab["dense"] == 2 * tokens * 2 * d * 2 + q_bytes + o_bytes
+    assert ab["sketch_topk"] == tokens * 2 * (d + 4) + bench.rerank_rows(wl, 2) * d * 2 + idx.numel() * 4 + q_bytes
