@@ -164,11 +164,11 @@ cs_status check_sketch(const cs_key_sketch* sk) {
   return CS_OK;
 }
 
-// Workspace of the sketch indexer (and, with `step`, of the fused step): candidate slots, sample
-// keys, slot counts, the query rows' codes and scales, the candidate lists (positions, scores),
-// then the selected lists of the step.
+// Workspace of the sketch indexer (and, with `step`, of the fused step): candidate slots (or every
+// sketch score), histograms of the full-score mode, slot counts, thresholds, the query rows'
+// codes and scales, the candidate lists (positions, scores), then the selected lists of the step.
 struct SketchWs {
-  size_t scores, hist, keys, counts, tau, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
+  size_t scores, hist, counts, tau, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
 };
 
 // Lists longer than 1/16 of the cache come from every sketch score (the candidate slots hold
@@ -186,8 +186,7 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
   SketchWs w;
   w.scores = 0;
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
-  w.keys = w.hist + (sketch_full(kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
-  w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
+  w.counts = w.hist + (sketch_full(kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
   w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.q_codes = w.tau + align_up(rows * sizeof(float));
   w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
@@ -200,7 +199,7 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
 }
 
 struct TopkWs {
-  size_t scores, hist, keys, counts, tau, total;
+  size_t scores, hist, counts, tau, total;
 };
 
 TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
@@ -210,8 +209,7 @@ TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
   TopkWs w;
   w.scores = 0;
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
-  w.keys = w.hist + align_up(rows * 4096 * sizeof(uint32_t));
-  w.counts = w.keys + align_up(rows * 1024 * sizeof(uint32_t));
+  w.counts = w.hist + align_up(rows * 4096 * sizeof(uint32_t));
   w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.total = w.tau + align_up(rows * sizeof(float));
   return w;
@@ -330,7 +328,6 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   a.score_stride = score_stride(shape, kv);
   a.scores = reinterpret_cast<float*>(ws + lay.scores);
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
-  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.tau = reinterpret_cast<float*>(ws + lay.tau);
   a.indices = indices;
@@ -415,7 +412,6 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
   a.scores = reinterpret_cast<float*>(ws + lay.scores);
   a.sketch_full = sketch_full(kv, k_max, cand_mult);
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
-  a.sample_keys = reinterpret_cast<uint32_t*>(ws + lay.keys);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.tau = reinterpret_cast<float*>(ws + lay.tau);
   a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);

@@ -38,7 +38,6 @@ struct TopkLaunch {
   int32_t* indices; // [rows, k_max]
   // filtered indexer (k_max <= max_len / 16): sampled thresholds, then candidates only
   bool filtered;
-  uint32_t* sample_keys;  // [rows, 1024]: ordered keys of the sampled scores
   uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
   float* tau;         // [rows]: candidate thresholds
   // fused decode step (filtered path): selection and attention per row in one kernel

@@ -553,10 +553,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // ============================================================================ filtered indexer
 // Writing every fp32 score and reading it back costs more than the 4 or 16 bytes per position
 // suggest (the writes interleave with the K stream), so for k <= N/16 the indexer avoids them:
-//  A. sample_keys_kernel scores a strided sample of at most kTauSamples positions per (request,
-//     KV head) and stores the ordered keys of each row's samples;
-//  B. tau_kernel sets, per row, a threshold tau: the 16-bit key prefix of the sample's r-th
-//     largest score, r ~ kCandFactor * k * (samples / visible).  score_cand_kernel then scores
+//  A. sample_tau_kernel scores a strided sample of at most kTauSamples positions per (request,
+//     KV head) and sets, per row, a threshold tau: the 16-bit key prefix of the sample's r-th
+//     largest score, r ~ kCandFactor * k * (samples / visible);
+//  B. score_cand_kernel then scores
 //     every position once, as score_hist_kernel does, and keeps only the candidates s >= tau as
 //     (position, score) pairs, staged in LDS and written a 128-byte line at a time into per-wave
 //     slots of the workspace.  A wave scans one contiguous range, so the slots concatenated in
@@ -568,98 +568,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //     those (exact, slow, rare).
 constexpr int kTauSamples = 1024;
 constexpr int kCandFactor = 3;
-constexpr int kTauParts = 4;                                       // workgroups per (request, KV head, row tile)
-constexpr int kTauWaves = 4;
-constexpr int kTauTilesPerWave = kTauSamples / kTauParts / 16 / kTauWaves;  // 4
-static_assert(kTauTilesPerWave * 16 * kTauWaves * kTauParts == kTauSamples, "sample tiling");
 
 // Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
 __device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L + kTauSamples - 1) / kTauSamples : 1; }
-
-// Ordered key of a sampled score; 0 marks "not a sample of this row" (every finite score has a
-// larger key).
-// SK: the scores are sketch scores (int8 codes of q and K, one MFMA step per 64 channels).
-template <int D, bool PAGED, bool SK>
-__global__ __launch_bounds__(kTauWaves * kWave) void sample_keys_kernel(
-    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
-    uint32_t* __restrict__ keys) {
-  constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
-  const int bh = blockIdx.x;
-  const int mt = blockIdx.y;
-  const int part = blockIdx.z;
-  const int Hkv = kv.num_kv_heads;
-  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
-  const int GT = G * T;
-  const int r0 = mt * 16;
-  const int rows_here = min(16, GT - r0);
-  const int L = seq_len_of(kv, b);
-  const int stride = tau_stride(L);
-  const int ns = (L + stride - 1) / stride;  // samples j * stride < L
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m = lane & 15;
-  const int g4 = lane >> 4;
-
-  uint4 a[KS];
-  {
-    const int r = r0 + m;
-    if (r < GT) {
-      const int t = r / G, gi = r - (r / G) * G;
-      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  // sample j = part * 256 + 16 * (wave * kTauTilesPerWave + u) + m at position j * stride
-  // (loads clamped to the last sample)
-  const int j0 = part * (kTauSamples / kTauParts) + 16 * wave * kTauTilesPerWave;
-  uint4 kt[kTauTilesPerWave][KS];
-  float ksc[kTauTilesPerWave];  // SK: the sampled rows' scales
-  const int jlast = max(ns - 1, 0);
-#pragma unroll
-  for (int u = 0; u < kTauTilesPerWave; ++u) {
-    const int j = min(j0 + 16 * u + m, jlast);
-    ksc[u] = 0.f;
-    if (L > 0) {
-      const int64_t off = kv_row<D, PAGED>(kv, b, h, j * stride);
-#pragma unroll
-      for (int kq = 0; kq < KS; ++kq)
-        kt[u][kq] = SK ? ld16i8(sk.codes + off + g4 * 16 + kq * 64) : ld16(kv.k + off + g4 * 8 + kq * 32);
-      if constexpr (SK) ksc[u] = sk.scales[off / D];
-    } else {
-#pragma unroll
-      for (int kq = 0; kq < KS; ++kq) kt[u][kq] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  int vis_i[4];
-  uint32_t* krow[4];
-  float qsc[4];  // SK: scales of this lane's output rows
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rl = 4 * g4 + i;
-    const int r = r0 + rl;
-    const int t = r / G, gi = r - (r / G) * G;
-    const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
-    vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
-    krow[i] = keys + (rl < rows_here ? qr * kTauSamples : 0);
-    qsc[i] = SK && rl < rows_here ? sk.q_scales[qr] : 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < kTauTilesPerWave; ++u) {
-    float sc[4];
-    tile_scores<SK, KS>(a, kt[u], scale, qsc, ksc[u], sc);
-    const int j = j0 + 16 * u + m;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = j < ns && j * stride < vis_i[i];
-      if (4 * g4 + i < rows_here) krow[i][j] = ok ? max(ord_key(sc[i]), 1u) : 0u;
-    }
-  }
-}
 
 // Candidate slots: wave w of workgroup (chunk c) of row `row` scans the positions
 // [c * chunk + w * chunk / kCandWaves, + chunk / kCandWaves) and owns slot s = c * kCandWaves + w
@@ -703,24 +614,102 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
   return key_to_float(P << 16);
 }
 
-// tau of every row (one wave per row) for score_cand_kernel; SK: for the row's
-// min(cand_mult * k', visible) largest sketch scores.
-template <bool SK>
-__global__ __launch_bounds__(4 * kWave) void tau_kernel(KVArgs kv, int T, int Hq, const int32_t* __restrict__ k_per_req,
-                                                       int k_max, int cand_mult, const uint32_t* __restrict__ sample_keys,
-                                                       float* __restrict__ tau, int rows) {
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int b = row / (T * Hq);
-  const int t = (row / Hq) - (row / (T * Hq)) * T;
+// A and the thresholds in one workgroup per (request, KV head, 16-row tile): kSampleWaves waves
+// score the kTauSamples sampled positions (sample j = 64 w + 16 u + m of wave w, tile u, lane
+// row m, at position j * stride; loads clamped to the last sample) against the tile's query rows
+// on MFMA and keep the samples' ordered keys in LDS (0 marks "not visible to this row"; every
+// finite score has a larger key); then wave w sets tau of the tile's row w with row_tau.
+// SK: sketch scores (int8 codes of q and K), and tau for the row's min(cand_mult * k', visible)
+// largest of them.
+constexpr int kSampleWaves = kTauSamples / 64;  // 16
+template <int D, bool PAGED, bool SK>
+__global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
+    const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
+    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ tau) {
+  extern __shared__ uint32_t lkeys[];  // [16][kTauSamples]
+  constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
+  constexpr int kTiles = 4;                 // 16-sample tiles per wave
+  const int bh = blockIdx.x;
+  const int mt = blockIdx.y;
+  const int Hkv = kv.num_kv_heads;
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int GT = G * T;
+  const int r0 = mt * 16;
+  const int rows_here = min(16, GT - r0);
   const int L = seq_len_of(kv, b);
-  const int vis = L - T + t + 1;
-  int kb = k_per_req ? k_per_req[b] : k_max;
-  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
-  const int kk = min(kb, max(vis, 0));
-  const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
-  const float th = row_tau(sample_keys + (int64_t)row * kTauSamples, vis, keep, tau_stride(L));
-  if ((threadIdx.x & 63) == 0) tau[row] = th;
+  const int stride = tau_stride(L);
+  const int ns = (L + stride - 1) / stride;  // samples j * stride < L
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+
+  uint4 a[KS];
+  {
+    const int r = r0 + m;
+    if (r < GT) {
+      const int t = r / G, gi = r - (r / G) * G;
+      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int j0 = 64 * wave;
+  uint4 kt[kTiles][KS];
+  float ksc[kTiles];  // SK: the sampled rows' scales
+  const int jlast = max(ns - 1, 0);
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    const int j = min(j0 + 16 * u + m, jlast);
+    ksc[u] = 0.f;
+    if (L > 0) {
+      const int64_t off = kv_row<D, PAGED>(kv, b, h, j * stride);
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq)
+        kt[u][kq] = SK ? ld16i8(sk.codes + off + g4 * 16 + kq * 64) : ld16(kv.k + off + g4 * 8 + kq * 32);
+      if constexpr (SK) ksc[u] = sk.scales[off / D];
+    } else {
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) kt[u][kq] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  int vis_i[4];
+  float qsc[4];  // SK: scales of this lane's output rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * g4 + i;
+    const int r = r0 + rl;
+    const int t = r / G, gi = r - (r / G) * G;
+    vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
+    qsc[i] = SK && rl < rows_here ? sk.q_scales[((int64_t)b * T + t) * Hq + (h * G + gi)] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    float sc[4];
+    tile_scores<SK, KS>(a, kt[u], scale, qsc, ksc[u], sc);
+    const int j = j0 + 16 * u + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = j < ns && j * stride < vis_i[i];
+      lkeys[(4 * g4 + i) * kTauSamples + j] = ok ? max(ord_key(sc[i]), 1u) : 0u;
+    }
+  }
+  __syncthreads();
+  if (wave < rows_here) {
+    const int r = r0 + wave;
+    const int t = r / G, gi = r - (r / G) * G;
+    const int vis = L - T + t + 1;
+    int kb = k_per_req ? k_per_req[b] : k_max;
+    kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+    const int kk = min(kb, max(vis, 0));
+    const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
+    const float th = row_tau(lkeys + wave * kTauSamples, vis, keep, stride);
+    if (lane == 0) tau[((int64_t)b * T + t) * Hq + (h * G + gi)] = th;
+  }
 }
 
 // Row mapping of the candidate pass: query row r of a 16-row tile sits in MFMA row
@@ -1375,7 +1364,7 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
 }
 
 // ============================================================================ reduced-byte indexer
-// C of the sketch pipeline (A and B are sample_keys_kernel / score_cand_kernel with SK): per row,
+// C of the sketch pipeline (A and B are sample_tau_kernel / score_cand_kernel with SK): per row,
 // the nc = min(cand_mult * k', visible) positions with the largest sketch scores (lower position
 // first among equal values) go to the row's list -- from the candidates, or from every sketch
 // score of the row when the candidates may not hold them (too few, or a slot overflowed), or
@@ -1628,11 +1617,13 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     if ((e = launch_full_select_t<D, PAGED, true>(a, a.cand_mult, a.list_stride, a.list_pos, stream)) != hipSuccess)
       return e;
   } else {
-    hipLaunchKernelGGL((sample_keys_kernel<D, PAGED, SK>), dim3(groups, tiles, kTauParts), dim3(kTauWaves * kWave),
-                       0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.sample_keys);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tau_kernel<SK>, dim3((a.rows + 3) / 4), dim3(4 * kWave), 0, stream, a.kv, a.T, a.Hq,
-                       a.k_per_req, a.k_max, a.cand_mult, a.sample_keys, a.tau, a.rows);
+    auto samp = sample_tau_kernel<D, PAGED, SK>;
+    const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
+    if ((e = hipFuncSetAttribute((const void*)samp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(samp, dim3(groups, tiles), dim3(kSampleWaves * kWave), lds_keys, stream, a.q, a.kv, a.sk,
+                       a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, a.cand_mult, a.tau);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
     const int rows_tile = a.GT < 16 ? a.GT : 16;
