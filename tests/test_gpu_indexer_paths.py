@@ -96,3 +96,10 @@ def test_filtered_long_lists_large_capacity_select():
     wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
                        seq_lens=[65536], k=3000, seed=46)
     _check_indexer(wl)
+
+
+def test_k_equals_max_len():
+    wl = make_workload(batch=2, q_len=2, num_q_heads=2, num_kv_heads=1, head_dim=128,
+                       seq_lens=[512, 300], k=512, max_len=512, seed=47)
+    idx = _check_indexer(wl)
+    assert idx[0, 1, :, :512].tolist() == [list(range(512))] * 2

@@ -191,3 +191,21 @@ def test_sketch_long_lists_large_capacity_select():
     wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
                        seq_lens=[65536], k=1500, seed=72)
     _run(wl, m=2, step=True)
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_sketch_full_score_paged_causal_d64(m):
+    # m * k > N / 16 on a paged cache with two query tokens: lists from every sketch score
+    wl = make_workload(batch=2, q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                       seq_lens=[3000, 1500], k=300, layout="paged", page_size=32, max_len=3008,
+                       seed=73)
+    _run(wl, m=m, step=(m == 2))
+
+
+def test_sketch_k_equals_max_len():
+    # k = N: every visible position is selected, on both the index-only and the fused paths
+    wl = make_workload(batch=2, q_len=2, num_q_heads=2, num_kv_heads=1, head_dim=128,
+                       seq_lens=[512, 300], k=512, max_len=512, seed=74)
+    idx = _run(wl, m=2)
+    assert idx[1, 0, :, :299].tolist() == [list(range(299))] * 2
+    _run(wl, m=1, step=True)
