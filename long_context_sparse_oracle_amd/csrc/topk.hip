@@ -614,13 +614,59 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
   return key_to_float(P << 16);
 }
 
+// SK: this lane's A operand of query row qrow -- the 16 values j * 64 + g4 * 16 .. + 16 of each
+// k-step j -- as int8 codes, quantised as the key sketch is: the row's maximum comes from the four
+// lanes m, m + 16, m + 32, m + 48 that hold it, scale = max / 127 and code = rint(x / scale),
+// both divisions correctly rounded, clamped to +-127; an invalid row gives zeros.  Returns the
+// row's scale.
+template <int D>
+__device__ __forceinline__ float quantize_q_operand(const uint16_t* __restrict__ qrow, bool valid, int g4,
+                                                    uint4 (&a)[D / 64]) {
+  constexpr int KS = D / 64;
+  float x[KS][16];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const uint4 lo = valid ? ld16(qrow + j * 64 + g4 * 16) : make_uint4(0, 0, 0, 0);
+    const uint4 hi = valid ? ld16(qrow + j * 64 + g4 * 16 + 8) : make_uint4(0, 0, 0, 0);
+    float f[8];
+    unpack8(lo, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[j][e] = f[e];
+    unpack8(hi, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[j][8 + e] = f[e];
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(x[j][e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float scale = __fdiv_rn(mx, 127.f);
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (scale > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float c = fminf(fmaxf(rintf(__fdiv_rn(x[j][e], scale)), -127.f), 127.f);
+        w[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
+      }
+    }
+    a[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return scale;
+}
+
 // A and the thresholds in one workgroup per (request, KV head, 16-row tile): kSampleWaves waves
 // score the kTauSamples sampled positions (sample j = 64 w + 16 u + m of wave w, tile u, lane
 // row m, at position j * stride; loads clamped to the last sample) against the tile's query rows
 // on MFMA and keep the samples' ordered keys in LDS (0 marks "not visible to this row"; every
 // finite score has a larger key); then wave w sets tau of the tile's row w with row_tau.
 // SK: sketch scores (int8 codes of q and K), and tau for the row's min(cand_mult * k', visible)
-// largest of them.
+// largest of them; the workgroup also quantises its query rows and stores their codes and scales
+// for the later passes.
 constexpr int kSampleWaves = kTauSamples / 64;  // 16
 template <int D, bool PAGED, bool SK>
 __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
@@ -645,14 +691,21 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
   const int g4 = lane >> 4;
 
   uint4 a[KS];
+  float my_qsc = 0.f;  // SK: scale of query row r0 + m
   {
     const int r = r0 + m;
-    if (r < GT) {
-      const int t = r / G, gi = r - (r / G) * G;
-      const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
+    const int t = r / G, gi = r - (r / G) * G;
+    const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
+    if constexpr (SK) {
+      my_qsc = quantize_q_operand<D>(q + (r < GT ? qr : 0) * D, r < GT, g4, a);
+      if (r < GT && wave == 0) {
 #pragma unroll
-      for (int j = 0; j < KS; ++j)
-        a[j] = SK ? ld16i8(sk.q_codes + qr * D + g4 * 16 + j * 64) : ld16(q + qr * D + g4 * 8 + j * 32);
+        for (int j = 0; j < KS; ++j) *reinterpret_cast<uint4*>(sk.q_codes + qr * D + g4 * 16 + j * 64) = a[j];
+        if (g4 == 0) sk.q_scales[qr] = my_qsc;
+      }
+    } else if (r < GT) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) a[j] = ld16(q + qr * D + g4 * 8 + j * 32);
     } else {
 #pragma unroll
       for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
@@ -685,7 +738,8 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int r = r0 + rl;
     const int t = r / G, gi = r - (r / G) * G;
     vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
-    qsc[i] = SK && rl < rows_here ? sk.q_scales[((int64_t)b * T + t) * Hq + (h * G + gi)] : 0.f;
+    qsc[i] = SK ? __shfl(my_qsc, rl) : 0.f;  // lane rl holds row r0 + rl's scale
+    (void)gi;
   }
 #pragma unroll
   for (int u = 0; u < kTiles; ++u) {
@@ -1607,10 +1661,10 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
   const int tiles = (a.GT + 15) / 16;
   const int groups = a.B * a.kv.num_kv_heads;
   hipError_t e;
-  if constexpr (SK) {
+  const bool listed = SK && a.sketch_full;
+  if (listed) {  // otherwise sample_tau_kernel quantises the query rows
     if ((e = launch_q_sketch(a.q, a.rows, D, a.sk.q_codes, a.sk.q_scales, stream)) != hipSuccess) return e;
   }
-  const bool listed = SK && a.sketch_full;
   if (listed && a.cand_mult == 1 && !a.fused)  // the selection is the sketch's own top-k
     return launch_full_select_t<D, PAGED, true>(a, 1, a.k_max, a.indices, stream);
   if (listed) {
