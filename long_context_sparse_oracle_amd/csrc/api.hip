@@ -366,9 +366,10 @@ cs::AttnLaunch sparse_launch(const cs_decode_shape* shape, const void* q, const 
 
 // ---- fused decode step: indexer + sparse attention in one call
 // Workspace: the indexer's, then the selected lists (int32 positions and float32 scores,
-// [rows, k_max] each), then the sparse attention's partials on the full-score path.
+// [rows, k_max] each; on the full-score path the positions only, when the caller passes no
+// index buffer).
 struct StepWs {
-  size_t topk, sel_pos, sel_score, attn, total;
+  size_t topk, sel_pos, sel_score, total;
 };
 
 StepWs step_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max) {
@@ -377,8 +378,7 @@ StepWs step_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_
   w.topk = 0;
   w.sel_pos = align_up(topk_ws(s, kv));
   w.sel_score = w.sel_pos + align_up(rows * (size_t)k_max * sizeof(int32_t));
-  w.attn = w.sel_score + align_up(rows * (size_t)k_max * sizeof(float));
-  w.total = w.attn + attn_ws(s, sparse_plan(s, k_max, 0).S);
+  w.total = w.sel_score + align_up(rows * (size_t)k_max * sizeof(float));
   return w;
 }
 
@@ -524,14 +524,14 @@ cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const 
     hipError_t e = cs::launch_topk(a, hs);
     return e == hipSuccess ? CS_OK : CS_ERR_HIP;
   }
-  // full-score path: the index lists (the caller's buffer, else the workspace), then attention
-  int32_t* idx = indices ? indices : sel_pos;
-  a.indices = idx;
+  // full-score path: the index lists (the caller's buffer, else the workspace), then the attention
+  // over them on the scores the indexer left in its workspace (V rows only)
+  a.indices = indices ? indices : sel_pos;
+  a.out = out;
+  a.lse = lse;
   hipError_t e = cs::launch_topk(a, hs);
   if (e != hipSuccess) return CS_ERR_HIP;
-  const SparsePlan plan = sparse_plan(shape, k_max, 0);
-  cs::AttnLaunch b = sparse_launch(shape, q, kv, idx, k_max, sm_scale, plan, out, lse, ws + lay.attn);
-  e = cs::launch_sparse(b, hs);
+  e = cs::launch_attend_scores(a, hs);
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
 }
 

@@ -78,6 +78,9 @@ size_t select_lds_bytes(int max_len);
 int score_threads(int GT);  // workgroup size of the score kernel for G*T query rows
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+// after launch_topk on the full-score path: attention of every row over its index list with the
+// scores the indexer left in a.scores (V rows only), into a.out / a.lse
+hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream);
 // int8 sketch of key rows [max(0, L_b - last_n), L_b) of every (request, KV head) (last_n <= 0:
 // all of [0, L_b)), and of `rows` contiguous query rows
 hipError_t launch_key_sketch(const KVArgs& kv, int B, int D, int last_n, int8_t* codes, float* scales,

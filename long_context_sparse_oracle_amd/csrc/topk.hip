@@ -1144,15 +1144,16 @@ __device__ void select_ordered(const Src& src, int total, int kk, int k_max, con
     for (int i = kk + tid; i < k_max; i += kCsThreads) so.idx[i] = -1;
 }
 
-// Attention of one row over its selected list (positions and scaled scores, kk entries), for the
-// fused decode step: the scores come with the list, so only V rows are read.  Each of the
+// Attention of one row over its selected list (kk positions; score_at(i, position) gives the
+// scaled score of entry i), for the fused decode step: the scores come with the list, so only V
+// rows are read.  Each of the
 // kCsWaves waves takes kCsAttnEntries entries per round (D/8 lanes per position, all V loads of
 // the round in flight before use), keeps an online softmax in log2 units, and the position groups
 // and waves are merged at the end (lane shuffles, then `red`: kCsWaves * (D + 2) floats of LDS).
 constexpr int kCsAttnEntries = 64;
-template <int D, bool PAGED>
+template <int D, bool PAGED, class ScoreAt>
 __device__ void attend_list(const KVArgs& kv, int b, int h, const int32_t* __restrict__ pos,
-                            const float* __restrict__ score, int kk, float* red,
+                            ScoreAt score_at, int kk, float* red,
                             float* __restrict__ out_row, float* __restrict__ lse_row) {
   constexpr int LPP = D / 8, PPW = kWave / LPP, NSTEP = kCsAttnEntries / PPW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1164,7 +1165,7 @@ __device__ void attend_list(const KVArgs& kv, int b, int h, const int32_t* __res
   for (int base = wave * kCsAttnEntries; base < kk; base += kCsWaves * kCsAttnEntries) {
     const bool mine_ok = base + lane < kk;
     const int my_pos = mine_ok ? pos[base + lane] : 0;
-    const float my_s = mine_ok ? score[base + lane] * kLog2e : -INFINITY;
+    const float my_s = mine_ok ? score_at(base + lane, my_pos) * kLog2e : -INFINITY;
     int idx[NSTEP];
     float sv[NSTEP];
 #pragma unroll
@@ -1412,9 +1413,34 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
   }
   if constexpr (FUSED) {
     __syncthreads();  // the selected list is complete, LDS free again
-    attend_list<D, PAGED>(kv, b, hq / G, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
+    const float* sel = so.score;
+    attend_list<D, PAGED>(kv, b, hq / G, so.pos, [sel](int i, int) { return sel[i]; }, kk,
+                          reinterpret_cast<float*>(smem),
                           out + (int64_t)row * D, lse + row);
   }
+}
+
+// The decode step on the full-score path (k > N/16): each row's index list (from select_kernel,
+// ascending) with the scores score_hist_kernel already wrote for every visible position, so the
+// attention gathers V rows only.  One workgroup per row.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kCsThreads) void attend_scores_kernel(
+    KVArgs kv, int T, int Hq, int G, const int32_t* __restrict__ k_per_req, int k_max,
+    const int32_t* __restrict__ indices, const float* __restrict__ scores, int64_t score_stride,
+    float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float red[kCsWaves * (D + 2)];
+  const int row = blockIdx.x;
+  const int b = row / (T * Hq);
+  const int t = (row / Hq) - (row / (T * Hq)) * T;
+  const int hq = row - (row / Hq) * Hq;
+  const int L = seq_len_of(kv, b);
+  const int vis = max(0, L - T + t + 1);
+  int kb = k_per_req ? k_per_req[b] : k_max;
+  kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+  const int kk = min(kb, vis);
+  const float* srow = scores + (int64_t)row * score_stride;
+  attend_list<D, PAGED>(kv, b, hq / G, indices + (int64_t)row * k_max, [srow](int, int p) { return srow[p]; }, kk,
+                        red, out + (int64_t)row * D, lse + row);
 }
 
 // ============================================================================ reduced-byte indexer
@@ -1593,7 +1619,8 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
   select_ordered(ListSource{lpos, lsc, rkey}, nc, kk, k_max, so, hist, sh, sh.kmin, sh.kmax);
   if constexpr (FUSED) {
     __syncthreads();  // the selected list is complete, LDS free again
-    attend_list<D, PAGED>(kv, b, h, so.pos, so.score, kk, reinterpret_cast<float*>(smem),
+    const float* sel = so.score;
+    attend_list<D, PAGED>(kv, b, h, so.pos, [sel](int i, int) { return sel[i]; }, kk, reinterpret_cast<float*>(smem),
                           out + (int64_t)row * D, lse + row);
   }
 }
@@ -1727,6 +1754,19 @@ static hipError_t launch_filtered(const TopkLaunch& a, hipStream_t stream) {
   if (a.D == 128)
     return a.paged ? launch_filtered_t<128, true, SK>(a, stream) : launch_filtered_t<128, false, SK>(a, stream);
   return a.paged ? launch_filtered_t<64, true, SK>(a, stream) : launch_filtered_t<64, false, SK>(a, stream);
+}
+
+hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(a.rows), dim3(kCsThreads), 0, stream, a.kv, a.T, a.Hq, a.G, a.k_per_req, a.k_max,
+                       a.indices, a.scores, a.score_stride, a.out, a.lse);
+  };
+  if (a.D == 128) {
+    if (a.paged) go(attend_scores_kernel<128, true>); else go(attend_scores_kernel<128, false>);
+  } else {
+    if (a.paged) go(attend_scores_kernel<64, true>); else go(attend_scores_kernel<64, false>);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
