@@ -136,9 +136,15 @@ int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv) {
 
 // The candidate pass addresses the rows of one (request, KV head) through a buffer resource,
 // whose size field is 32-bit: their score areas must span less than 2 GiB.
+// The candidate selection holds about 4.5 k candidates of a row in LDS: 12288 keys, or 24576 when
+// there are no more rows than compute units (one workgroup per unit).  Longer lists would take
+// its slow global-memory path, so they use the full-score path instead.
+int64_t cand_lds_keys(const cs_decode_shape* s) { return rows_of(s) <= cu_count() ? 24576 : 12288; }
+
 bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
   const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
-  return (int64_t)k_max * 16 <= kv->max_len && span < (1LL << 31);
+  return (int64_t)k_max * 16 <= kv->max_len && (int64_t)k_max * 9 / 2 <= cand_lds_keys(s) &&
+         span < (1LL << 31);
 }
 
 // ---- reduced-byte indexer sizing
@@ -172,9 +178,10 @@ struct SketchWs {
 };
 
 // Lists longer than 1/16 of the cache come from every sketch score (the candidate slots hold
-// about half of a chunk's positions).
-bool sketch_full(const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
-  return (int64_t)cand_mult * k_max * 16 > kv->max_len;
+// about half of a chunk's positions), as do lists whose candidates would not fit in LDS.
+bool sketch_full(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
+  const int64_t keep = (int64_t)cand_mult * k_max;
+  return keep * 16 > kv->max_len || keep * 9 / 2 > cand_lds_keys(s);
 }
 
 SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult,
@@ -186,7 +193,7 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
   SketchWs w;
   w.scores = 0;
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
-  w.counts = w.hist + (sketch_full(kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
+  w.counts = w.hist + (sketch_full(s, kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
   w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.q_codes = w.tau + align_up(rows * sizeof(float));
   w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
@@ -410,7 +417,7 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
   a.sk.q_codes = reinterpret_cast<int8_t*>(ws + lay.q_codes);
   a.sk.q_scales = reinterpret_cast<float*>(ws + lay.q_scales);
   a.scores = reinterpret_cast<float*>(ws + lay.scores);
-  a.sketch_full = sketch_full(kv, k_max, cand_mult);
+  a.sketch_full = sketch_full(shape, kv, k_max, cand_mult);
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.tau = reinterpret_cast<float*>(ws + lay.tau);
