@@ -137,13 +137,14 @@ int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv) {
 // The candidate pass addresses the rows of one (request, KV head) through a buffer resource,
 // whose size field is 32-bit: their score areas must span less than 2 GiB.
 // The candidate selection holds about 4.5 k candidates of a row in LDS: 12288 keys, or 24576 when
-// there are no more rows than compute units (one workgroup per unit).  Longer lists would take
-// its slow global-memory path, so they use the full-score path instead.
+// there are no more rows than compute units (one workgroup per unit); rows with more use its
+// global-memory path.  When even half of such lists would not fit (k_max sizes the lists, the
+// rows of a ragged batch mostly ask for fewer), the full-score path is used instead.
 int64_t cand_lds_keys(const cs_decode_shape* s) { return rows_of(s) <= cu_count() ? 24576 : 12288; }
 
 bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
   const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
-  return (int64_t)k_max * 16 <= kv->max_len && (int64_t)k_max * 9 / 2 <= cand_lds_keys(s) &&
+  return (int64_t)k_max * 16 <= kv->max_len && (int64_t)k_max * 9 / 2 <= 2 * cand_lds_keys(s) &&
          span < (1LL << 31);
 }
 
@@ -181,7 +182,7 @@ struct SketchWs {
 // about half of a chunk's positions), as do lists whose candidates would not fit in LDS.
 bool sketch_full(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
   const int64_t keep = (int64_t)cand_mult * k_max;
-  return keep * 16 > kv->max_len || keep * 9 / 2 > cand_lds_keys(s);
+  return keep * 16 > kv->max_len || keep * 9 / 2 > 2 * cand_lds_keys(s);
 }
 
 SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult,
