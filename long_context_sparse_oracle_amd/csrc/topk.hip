@@ -1,5 +1,10 @@
-// Oracle top-k indexer for gfx950: a streaming score kernel (q.K^T on MFMA, fused 12-bit
-// radix histogram) and a per-row select kernel (LDS radix refinement, ballot compaction).
+// Oracle top-k indexer for gfx950, and the parts of the decode step that sit on its scores.
+//  * full-score path: a streaming score kernel (q.K^T on MFMA, fused 12-bit radix histogram) and
+//    a per-row select kernel (LDS radix refinement, ballot compaction);
+//  * candidate path (short lists): sampled thresholds, a streaming pass that keeps only the
+//    candidates above them, and a per-row radix select over the candidates;
+//  * the one-call step's attention on the selected lists with the indexer's own scores;
+//  * the reduced-byte indexer: the same passes on an int8 key sketch, then an exact re-rank.
 //
 // Method: exact top-k selection of cached tokens per (request, token, query head), as used by the
 // oracle indexer of "Inference Time Context Sparsity: Illusion or Opportunity?" (technical
