@@ -7,7 +7,8 @@ include/ctxsparse.h); this package is a thin ctypes binding with the same entry-
     sparse_decode_attn(q, cache, indices)   -> (out fp32 [B, T, Hq, d], lse fp32 [B, T, Hq])
     dense_decode_attn(q, cache)             -> (out, lse) over every visible position
     sparse_decode_step(q, cache, k)         -> (out, lse): the indexer and the sparse attention
-                                               in one call (fused per row for k <= N/16)
+                                               in one call, the attention on the indexer's own
+                                               scores (V rows gathered only)
     key_sketch_build(cache)                 -> KeySketch: int8 codes + float32 scale per key row
     topk_index_sketch(q, cache, sketch, k)  -> the reduced-byte indexer: cand_mult * k candidates
                                                ranked on the sketch, re-ranked on exact scores

@@ -363,9 +363,9 @@ def sparse_decode_step(
     lse: Optional[torch.Tensor] = None,
     workspace: Optional[torch.Tensor] = None,
 ):
-    """The oracle-indexed decode step in one call (topk_index, then sparse_decode_attn over its
-    lists): returns (out, lse), or (out, lse, indices) with return_indices or an `indices`
-    tensor given."""
+    """The oracle-indexed decode step in one call (the results of topk_index and of
+    sparse_decode_attn over its lists, the attention computed on the indexer's scores): returns
+    (out, lse), or (out, lse, indices) with return_indices or an `indices` tensor given."""
     shp = _shape(q, cache)
     k, kptr, k_max = _k_arg(k, k_max, shp, q.device)
     if indices is None and return_indices:
