@@ -223,3 +223,42 @@ def test_error_status_raises():
                        seq_lens=[100], k=10, seed=33).to("cuda")
     with pytest.raises(m.CtxSparseError):
         m.topk_index(wl.q, cache_of(wl), 101)  # k_max above max_len
+
+
+def test_paged_equals_contiguous_every_entry_point():
+    """The same logical cache stored paged (permuted pages) and contiguously gives the same index
+    lists (the scores are bit-identical) and the same outputs, on every entry point."""
+    m = _lib()
+    wl = make_workload(batch=3, q_len=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       seq_lens=[5000, 1234, 3000], k=0.02, layout="paged", page_size=16, max_len=5008,
+                       needles_per_head=2, seed=33).to("cuda")
+    B, Hkv, d, L = wl.batch, wl.num_kv_heads, wl.head_dim, wl.max_len
+    kc = torch.zeros((B, Hkv, L, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for b in range(B):
+        n = torch.arange(int(wl.seq_lens[b]), device="cuda")
+        pages = wl.page_table[b, n // 16].long()
+        kc[b, :, : n.numel()] = wl.k_cache[pages, :, n % 16].transpose(0, 1)
+        vc[b, :, : n.numel()] = wl.v_cache[pages, :, n % 16].transpose(0, 1)
+    paged = cache_of(wl)
+    contig = m.KVCache(kc, vc, wl.seq_lens, max_len=L)
+    res = {}
+    for name, cache in (("paged", paged), ("contiguous", contig)):
+        idx = m.topk_index(wl.q, cache, wl.k_per_req, k_max=wl.k_max)
+        o, l = m.sparse_decode_attn(wl.q, cache, idx)
+        od, ld = m.dense_decode_attn(wl.q, cache)
+        os_, ls_, is_ = m.sparse_decode_step(wl.q, cache, wl.k_per_req, k_max=wl.k_max, return_indices=True)
+        sk = m.key_sketch_build(cache)
+        ok, lk, ik = m.sparse_decode_step_sketch(wl.q, cache, sk, wl.k_per_req, k_max=wl.k_max, cand_mult=2,
+                                                 return_indices=True)
+        torch.cuda.synchronize()
+        res[name] = (idx, o, l, od, ld, os_, ls_, is_, ok, lk, ik)
+    names = ("idx", "sparse o", "sparse lse", "dense o", "dense lse", "step o", "step lse", "step idx",
+             "sketch o", "sketch lse", "sketch idx")
+    for n, a, c in zip(names, res["paged"], res["contiguous"]):
+        if a.dtype == torch.int32:
+            assert torch.equal(a, c), n
+        else:
+            fin = torch.isfinite(c)
+            assert torch.equal(torch.isfinite(a), fin), n
+            assert float((a[fin] - c[fin]).abs().max()) <= 1e-5, n
