@@ -237,6 +237,19 @@ struct SelShared {
   uint32_t found;
 };
 
+// Folds this thread's key range into sh.kmin / sh.kmax (which start at ~0 / 0): reduced over the
+// wave first, so one lane per wave issues the LDS atomics (the compiler otherwise serialises a
+// same-address atomic through a 64-step loop on the scalar unit that the CU's waves share).  All
+// lanes of the wave take part.
+__device__ __forceinline__ void block_key_range(uint32_t lmin, uint32_t lmax, SelShared& sh) {
+  lmin = wave_min_u32(lmin);
+  lmax = wave_max_u32(lmax);
+  if ((threadIdx.x & 63) == 0) {
+    atomicMin(&sh.kmin, lmin);
+    atomicMax(&sh.kmax, lmax);
+  }
+}
+
 // Finds, over `nbins` counters hist[0..nbins) (bin nbins-1 highest), the bin holding the need-th
 // largest key.  Each of the NW * 64 threads covers PER = nbins / (NW * 64) consecutive bins,
 // highest bins on thread 0.  Returns the total count.
@@ -694,6 +707,8 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int g4 = lane >> 4;
+  // the request's k, read now so that its latency overlaps the sample loads
+  const int k_req = k_per_req ? k_per_req[b] : k_max;
 
   uint4 a[KS];
   float my_qsc = 0.f;  // SK: scale of query row r0 + m
@@ -762,8 +777,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int r = r0 + wave;
     const int t = r / G, gi = r - (r / G) * G;
     const int vis = L - T + t + 1;
-    int kb = k_per_req ? k_per_req[b] : k_max;
-    kb = kb < 0 ? 0 : (kb > k_max ? k_max : kb);
+    const int kb = k_req < 0 ? 0 : (k_req > k_max ? k_max : k_req);
     const int kk = min(kb, max(vis, 0));
     const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
     const float th = row_tau(lkeys + wave * kTauSamples, vis, keep, stride);
@@ -1292,8 +1306,7 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
       }
     }
   }
-  atomicMin(&sh.kmin, lmin);
-  atomicMax(&sh.kmax, lmax);
+  block_key_range(lmin, lmax, sh);
   __syncthreads();
   uint32_t need, cnt_eq;
   const uint32_t kstar = radix_kth([&](int f) { return lds_key[f]; }, (int)total, kk, sh.kmin, sh.kmax,
@@ -1537,8 +1550,7 @@ __device__ void rerank_exact(const KVArgs& kv, int b, int h, const uint16_t* __r
     }
     my = nxt;
   }
-  atomicMin(&sh.kmin, lmin);
-  atomicMax(&sh.kmax, lmax);
+  block_key_range(lmin, lmax, sh);
 }
 
 // list_pos / list_score: the rows' lists (list_stride >= min(cand_mult * k_max, max_len) entries);
