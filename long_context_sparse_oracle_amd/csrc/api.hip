@@ -226,10 +226,8 @@ TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
 size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) { return topk_ws_layout(s, kv).total; }
 
 // ---- attention sizing
-// Gather plan.  A wave handles one round of E index entries.  When every wave of the call fits
-// on the GPU at once (12 per CU at E = 64), whole lists go to single workgroups of up to 12
-// waves (no partials to merge).  Larger calls use E = 32 and 4-wave workgroups, several per CU,
-// so load and compute phases of different workgroups overlap.
+// Gather plan: splits per row, entries per split, waves per workgroup (a wave takes
+// kSparseWaveEntries entries per round).
 struct SparsePlan {
   int S, chunk, waves;
 };
