@@ -18,8 +18,10 @@ drawn on the GPU before the timed region.
 Prints ONE JSON line.  `value` is the sparse decode attention's gathered-KV throughput: the
 distinct K/V rows the step's index lists name (counted once per (request, KV head) group, 512 B
 each at d=128) plus index, query and output bytes, divided by the mean duration of the
-sparse_decode_attn call.  Also reported: µs of every call, speedup over the dense decode on the
-same inputs, a roofline object per kernel and the CPU oracle timed on the host cores.
+sparse_decode_attn call.  Also reported: µs of every call (mean, and p10/p50/p90), speedup over
+the dense decode on the same inputs, a roofline object per kernel and the CPU oracle timed on the
+host cores; beside the timed steps, the sparse call on uniform random index sets of the same
+sizes (cold) and warm-cache timings of the main calls.
 Call durations come from HIP events created with hipEventDisableSystemFence; an event pair
 around one call still counts about 4 µs of dispatch latency on top of the kernels' run time.
 """
@@ -162,6 +164,25 @@ def recall(idx_a, idx_b, max_len):
     return hit / total if total else 1.0
 
 
+def percentiles(values):
+    """p10, p50, p90 of a list of timings (linear interpolation between order statistics)."""
+    import numpy as np
+
+    return [round(float(x), 2) for x in np.percentile(np.asarray(values, dtype=np.float64), [10, 50, 90])]
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def cpu_baseline(wl, gathered_bytes, seconds):
     """The CPU oracle (top-k + sparse attention per row) timed on the host on a bounded sample
     of the same workload, scaled to the full step."""
@@ -218,6 +239,8 @@ def cpu_baseline(wl, gathered_bytes, seconds):
         "value": round(gathered_bytes / step_s / 1e9, 4),
         "unit": "GB/s",
         "cores": int(cores),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "us_per_step": round(step_s * 1e6, 1),
         "sample": (
@@ -413,8 +436,41 @@ def main():
         hev.destroy(e1)
 
     ab = algorithmic_bytes(wl, indices, m)
-    # one full build of the sketch (every cached key), timed on its own after the steps
     hev2 = HipEvents()
+
+    def timed(fn, n, cold):
+        """Mean µs of n back-to-back calls of fn between fence-free events (each after a flush when
+        cold), synchronised once at the end as the timed steps are."""
+        evs = [(hev2.create(), hev2.create()) for _ in range(n)]
+        for e0, e1 in evs:
+            if cold:
+                flush()
+            hev2.record(e0, sh)
+            fn()
+            hev2.record(e1, sh)
+        torch.cuda.synchronize()
+        ts = [hev2.elapsed_us(e0, e1) for e0, e1 in evs]
+        for e0, e1 in evs:
+            hev2.destroy(e0)
+            hev2.destroy(e1)
+        return statistics.fmean(ts)
+
+    # Beside the timed steps (not part of `value`): the sparse call on uniform random index sets of
+    # the same sizes (drawn without replacement), cold; and warm-cache timings of the main calls.
+    from workloads import random_index_sets
+
+    idx_rand = random_index_sets(wl)
+    ab_rand = algorithmic_bytes(wl, idx_rand, m)
+    rand_us = timed(lambda: cs.sparse_decode_attn(wl.q, cache, idx_rand, num_splits=args.sparse_splits,
+                                                  out=out_s, lse=lse_s, workspace=ws_s), max(args.steps, 5), True)
+    rand_gbs = ab_rand["sparse"] / (rand_us * 1e-6) / 1e9
+    warm = None
+    if flush_buf is not None:
+        warm = {}
+        for name in ("topk_index", "sparse_decode_attn", "dense_decode_attn", "sparse_decode_step"):
+            calls[name]()
+            warm[name] = round(timed(calls[name], 5, False), 2)
+    # one full build of the sketch (every cached key), timed on its own after the steps
     eb0, eb1 = hev2.create(), hev2.create()
     flush()
     hev2.record(eb0, sh)
@@ -482,6 +538,15 @@ def main():
             "rerank_rows": ab["rerank_rows"],
         },
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
+        "percentiles_us": {name: percentiles(v) for name, v in times.items()},
+        "random_sets": {
+            "sparse_us": round(rand_us, 2),
+            "gathered_bytes": ab_rand["sparse"],
+            "gbs": round(rand_gbs, 1),
+            "pct_hbm_peak": round(100.0 * rand_gbs / HBM_PEAK_GBS, 2),
+            "speedup_vs_dense": round(mean["dense_decode_attn"] / rand_us, 3),
+        },
+        "warm_us": warm,
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
         "algorithmic_bytes": {"topk_index": ab["topk"], "sparse_decode_attn": ab["sparse"],

@@ -44,3 +44,14 @@ def test_algorithmic_bytes_distinct_rows():
     tokens = 110
     assert ab["dense"] == 2 * tokens * 2 * d * 2 + q_bytes + o_bytes
     assert ab["sketch_topk"] == tokens * 2 * (d + 4) + bench.rerank_rows(wl, 2) * d * 2 + idx.numel() * 4 + q_bytes
+
+
+def test_percentiles_linear_interpolation():
+    # p10/p50/p90 of 0..10 are 1, 5, 9; of a constant list the constant
+    assert bench.percentiles(list(range(11))) == [1.0, 5.0, 9.0]
+    assert bench.percentiles([3.5] * 4) == [3.5, 3.5, 3.5]
+
+
+def test_cpu_model_is_text_or_none():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
