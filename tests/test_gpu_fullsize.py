@@ -1,5 +1,7 @@
 """GPU parity at the named workloads' full sizes, in the launch configuration bench.py times
-(automatic splits and chunking), including the sweep's 500x point and its 64-request batch.
+(automatic splits and chunking), including the sweep's 500x point and its 64-request batch, and
+at the library's documented limits (262144 positions on both indexer paths, 64 query rows per KV
+head, 4096-position pages, head_dim 64 at a long context).
 
 * Sampled rows (first, last and seeded random ones) are compared with the CPU oracle one by one:
   indexer by the band rule, sparse attention fed the oracle's own index lists, dense attention;
@@ -222,3 +224,53 @@ def test_sweep_b64_n128k_500x():
 def test_ragged_paged_b32_t4():
     wl = make_named("ragged_paged_b32_t4", device="cuda")
     _run(wl, seed=14)
+
+
+# ---- the documented limits: max_len = 262144 (the exact indexer's bound) on both indexer paths,
+# 64 query rows per KV head, the largest page size, head_dim 64 at a long context
+
+def test_max_len_limit_filtered():
+    """262144 positions, k = N/50: the candidate path (k * 16 <= N)."""
+    from workloads import make_workload
+
+    wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[262144],
+                       k=5242, needles_per_head=4, seed=41, device="cuda")
+    _run(wl, seed=41)
+
+
+def test_max_len_limit_full_score():
+    """262144 positions, k = N/8: the full-score path (every score, histogram select)."""
+    from workloads import make_workload
+
+    wl = make_workload(batch=1, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=128, seq_lens=[262144],
+                       k=32768, needles_per_head=2, seed=42, device="cuda")
+    _run(wl, seed=42)
+
+
+def test_64_query_rows_per_kv_head_paged():
+    """G * T = 64 (G = 16, T = 4): four 16-row tiles per KV head, ragged paged requests."""
+    from workloads import make_workload
+
+    wl = make_workload(batch=2, q_len=4, num_q_heads=16, num_kv_heads=1, head_dim=128,
+                       seq_lens=[20000, 9001], k=0.02, layout="paged", page_size=16, max_len=20000,
+                       needles_per_head=2, seed=43, device="cuda")
+    _run(wl, seed=43)
+
+
+def test_64_query_heads_on_one_kv_head_page_4096():
+    """G = 64 at T = 1, pages of 4096 positions (the largest page size)."""
+    from workloads import make_workload
+
+    wl = make_workload(batch=2, q_len=1, num_q_heads=64, num_kv_heads=1, head_dim=128,
+                       seq_lens=[40000, 12289], k=0.02, layout="paged", page_size=4096, max_len=40960,
+                       needles_per_head=2, seed=44, device="cuda")
+    _run(wl, seed=44)
+
+
+def test_head_dim_64_long_context():
+    """d = 64 at 65536 positions, G = 1, k = N/100."""
+    from workloads import make_workload
+
+    wl = make_workload(batch=2, q_len=1, num_q_heads=8, num_kv_heads=8, head_dim=64, seq_lens=[65536, 50000],
+                       k=655, needles_per_head=2, seed=45, device="cuda")
+    _run(wl, seed=45)
