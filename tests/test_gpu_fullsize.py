@@ -274,3 +274,31 @@ def test_head_dim_64_long_context():
     wl = make_workload(batch=2, q_len=1, num_q_heads=8, num_kv_heads=8, head_dim=64, seq_lens=[65536, 50000],
                        k=655, needles_per_head=2, seed=45, device="cuda")
     _run(wl, seed=45)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_attention_one_million_positions(layout):
+    """sparse_decode_attn and dense_decode_attn (no length bound of their own) at 2**20 positions,
+    two query tokens (causal), uniform random index sets of 2% of the row: sampled rows against
+    the oracle."""
+    from workloads import make_workload
+
+    m = _lib()
+    L = 1 << 20
+    wl = make_workload(batch=1, q_len=2, num_q_heads=4, num_kv_heads=1, head_dim=128, seq_lens=[L],
+                       k=L // 50, layout=layout, page_size=64, seed=46, device="cuda")
+    cache = _cache(wl)
+    sets = random_index_sets(wl, seed=47)
+    o, l = m.sparse_decode_attn(wl.q, cache, sets)
+    od, ld = m.dense_decode_attn(wl.q, cache)
+    torch.cuda.synchronize()
+    o, l, od, ld = o.cpu().numpy(), l.cpu().numpy(), od.cpu().numpy(), ld.cpu().numpy()
+    sets_cpu = sets.cpu().numpy()
+    q = oracle.bf16_bits_to_f64(bits(wl.q))
+    K, V = logical_kv(wl, 0, 0)
+    for t, hq in ((0, 0), (1, 3), (1, 1)):
+        vis = oracle.visible_length(L, wl.q_len, t)
+        want = oracle.row_sparse(q[0, t, hq], K, V, sets_cpu[0, t, hq], vis)
+        check_attn_row(o[0, t, hq], l[0, t, hq], want[0], want[1], f"sparse {(t, hq)}")
+        want = oracle.row_dense(q[0, t, hq], K, V, vis)
+        check_attn_row(od[0, t, hq], ld[0, t, hq], want[0], want[1], f"dense {(t, hq)}")
