@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--sparse-splits", type=int, default=0)
     p.add_argument("--dense-splits", type=int, default=0)
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the reported figure)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the random-set and warm-cache timings after the steps (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle leg (0 disables it)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -162,6 +164,10 @@ def recall(idx_a, idx_b, max_len):
         hit += int(torch.gather(ma, 1, torch.where(vb < 0, max_len, vb)).sum())
     total = int((bb >= 0).sum())
     return hit / total if total else 1.0
+
+
+def mean_of(values):
+    return statistics.fmean(values)
 
 
 def percentiles(values):
@@ -459,13 +465,22 @@ def main():
     # the same sizes (drawn without replacement), cold; and warm-cache timings of the main calls.
     from workloads import random_index_sets
 
-    idx_rand = random_index_sets(wl)
-    ab_rand = algorithmic_bytes(wl, idx_rand, m)
-    rand_us = timed(lambda: cs.sparse_decode_attn(wl.q, cache, idx_rand, num_splits=args.sparse_splits,
-                                                  out=out_s, lse=lse_s, workspace=ws_s), max(args.steps, 5), True)
-    rand_gbs = ab_rand["sparse"] / (rand_us * 1e-6) / 1e9
+    random_sets = None
+    if not args.no_extras:
+        idx_rand = random_index_sets(wl)
+        ab_rand = algorithmic_bytes(wl, idx_rand, m)
+        rand_us = timed(lambda: cs.sparse_decode_attn(wl.q, cache, idx_rand, num_splits=args.sparse_splits,
+                                                      out=out_s, lse=lse_s, workspace=ws_s), max(args.steps, 5), True)
+        rand_gbs = ab_rand["sparse"] / (rand_us * 1e-6) / 1e9
+        random_sets = {
+            "sparse_us": round(rand_us, 2),
+            "gathered_bytes": ab_rand["sparse"],
+            "gbs": round(rand_gbs, 1),
+            "pct_hbm_peak": round(100.0 * rand_gbs / HBM_PEAK_GBS, 2),
+            "speedup_vs_dense": round(mean_of(times["dense_decode_attn"]) / rand_us, 3),
+        }
     warm = None
-    if flush_buf is not None:
+    if flush_buf is not None and not args.no_extras:
         warm = {}
         for name in ("topk_index", "sparse_decode_attn", "dense_decode_attn", "sparse_decode_step"):
             calls[name]()
@@ -539,13 +554,7 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
         "percentiles_us": {name: percentiles(v) for name, v in times.items()},
-        "random_sets": {
-            "sparse_us": round(rand_us, 2),
-            "gathered_bytes": ab_rand["sparse"],
-            "gbs": round(rand_gbs, 1),
-            "pct_hbm_peak": round(100.0 * rand_gbs / HBM_PEAK_GBS, 2),
-            "speedup_vs_dense": round(mean["dense_decode_attn"] / rand_us, 3),
-        },
+        "random_sets": random_sets,
         "warm_us": warm,
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
