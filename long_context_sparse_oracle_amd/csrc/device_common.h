@@ -170,23 +170,6 @@ __device__ __forceinline__ int64_t kv_row(const KVArgs& kv, int b, int h, int n)
   }
 }
 
-// Same, for a 16-aligned tile start n0 that is uniform across the wave (every position of the
-// tile lies in one page because page sizes are powers of two >= 16): the page id is read with a
-// scalar load; returns the offset of row n0, rows n0 + j follow at + j*D.
-template <int D, bool PAGED>
-__device__ __forceinline__ int64_t kv_tile(const KVArgs& kv, int b, int h, int n0) {
-  n0 = __builtin_amdgcn_readfirstlane(n0);
-  if constexpr (!PAGED) {
-    return ((int64_t)(b * kv.num_kv_heads + h) * kv.max_len + n0) * D;
-  } else {
-    int page = __builtin_amdgcn_readfirstlane(
-        kv.page_table[(int64_t)b * kv.max_pages + (n0 >> kv.page_shift)]);
-    page = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
-    const int slot = n0 & ((1 << kv.page_shift) - 1);
-    return ((((int64_t)page * kv.num_kv_heads + h) << kv.page_shift) + slot) * D;
-  }
-}
-
 // Page ids of logical positions [start, end) of request b, clamped to the pool, copied into LDS
 // by the whole workgroup (paged caches only; the caller synchronises before use).  Entry i holds
 // the page of position ((start >> page_shift) + i) << page_shift.
