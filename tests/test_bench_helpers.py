@@ -55,3 +55,34 @@ def test_percentiles_linear_interpolation():
 def test_cpu_model_is_text_or_none():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+def test_profile_harness_groups_and_names_calls():
+    import bench_profile as bp
+
+    def row(name, t):
+        return {"Kernel_Name": name, "Start_Timestamp": str(t), "End_Timestamp": str(t + 1000)}
+
+    flush = "void at::native::reduce_kernel<512, 1>(...)"
+    seq = ["void cs::key_sketch_kernel<128, false>(...)",  # the full build before the steps
+           flush, "void cs::sample_tau_kernel<128, false, false>(...)", "void cs::score_cand_kernel<128, false, 1, false>(...)",
+           "void cs::cand_select_kernel<128, false, false, 3>(...)",
+           flush, "void cs::sparse_partial_kernel<128, false, 16, 8>(...)",
+           flush, "void cs::dense_partial_kernel<128, false, 4>(...)", "cs::combine_kernel(...)",
+           flush, "void cs::sample_tau_kernel<128, false, false>(...)", "void cs::score_cand_kernel<128, false, 1, false>(...)",
+           "void cs::cand_select_kernel<128, false, true, 3>(...)",
+           flush, "void cs::score_hist_kernel<128, false, false>(...)", "void cs::select_kernel(...)",
+           "void cs::attend_scores_kernel<128, false>(...)",
+           flush, "void cs::key_sketch_kernel<128, false>(...)",
+           flush, "void cs::sample_tau_kernel<128, false, true>(...)", "void cs::score_cand_kernel<128, false, 1, true>(...)",
+           "void cs::sketch_select_kernel<128, false, false, 3>(...)",
+           flush, "void cs::sketch_select_kernel<128, false, true, 3>(...)",
+           flush, "void cs::key_sketch_kernel<128, false>(...)"]  # the timed full build after the steps
+    rows = [row(n, 10000 * i) for i, n in enumerate(seq)]
+    segs = bp.segments(rows, lambda r: 1.0)
+    assert [e for e, _ in segs] == ["key_sketch_build", "topk_index", "sparse_decode_attn", "dense_decode_attn",
+                                    "sparse_decode_step", "sparse_decode_step", "key_sketch_update",
+                                    "topk_index_sketch", "sparse_decode_step_sketch", "key_sketch_build"]
+    assert segs[1][1] == {"cs::sample_tau_kernel<128, false, false>": 1.0,
+                          "cs::score_cand_kernel<128, false, 1, false>": 1.0,
+                          "cs::cand_select_kernel<128, false, false, 3>": 1.0}
