@@ -235,14 +235,18 @@ struct SparsePlan {
 SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
   // One workgroup of up to kSparseWaves waves per row, looping over its list kSparseWaveEntries
   // entries per wave and round: no partials and no combine pass.  Only when there are fewer rows
-  // than compute units are lists split, to put every unit to work.
+  // than compute units are lists split, to put every unit to work, and only lists that take more
+  // than one round of a workgroup (splitting a one-round list shortens nothing and adds the
+  // combine pass).
   const int64_t rows = rows_of(s);
   const int64_t waves_needed = ceil_div(k_max, cs::kSparseWaveEntries);
   int64_t S;
   if (requested > 0) {
     S = requested;
+  } else if (rows >= cu_count() || waves_needed <= cs::kSparseWaves) {
+    S = 1;
   } else {
-    S = rows >= cu_count() ? 1 : ceil_div(cu_count(), rows);
+    S = ceil_div(cu_count(), rows);
     if (S > waves_needed) S = waves_needed;
   }
   if (S > k_max) S = k_max;
