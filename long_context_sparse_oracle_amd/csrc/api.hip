@@ -333,6 +333,8 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   topk_chunking(shape, kv, &a.chunk, &a.chunks);
   cand_chunking(shape, kv, &a.cand_chunk, &a.cand_chunks);
   a.filtered = topk_filtered(shape, kv, k_max);
+  a.small = kv->max_len <= cs::kTauSamples;  // every position is scored and selected in one kernel
+  a.keep_scores = false;
   char* ws = static_cast<char*>(workspace);
   const TopkWs lay = topk_ws_layout(shape, kv);
   a.score_stride = score_stride(shape, kv);
@@ -413,6 +415,7 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
                              const SketchWs& lay) {
   cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws);
   a.filtered = true;
+  a.small = false;
   a.sketch = true;
   a.cand_mult = cand_mult;
   a.sk.codes = static_cast<const int8_t*>(sketch->codes);
@@ -524,7 +527,7 @@ cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int32_t* sel_pos = reinterpret_cast<int32_t*>(ws + lay.sel_pos);
   cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws + lay.topk);
-  if (a.filtered) {
+  if (a.filtered && !a.small) {
     // selection and attention of a row in one workgroup, on the candidates' own scores
     a.fused = true;
     a.sel_pos = sel_pos;
@@ -534,9 +537,11 @@ cs_status sparse_decode_step(const cs_decode_shape* shape, const void* q, const 
     hipError_t e = cs::launch_topk(a, hs);
     return e == hipSuccess ? CS_OK : CS_ERR_HIP;
   }
-  // full-score path: the index lists (the caller's buffer, else the workspace), then the attention
-  // over them on the scores the indexer left in its workspace (V rows only)
+  // full-score path (or a cache short enough to be scored whole in one kernel): the index lists
+  // (the caller's buffer, else the workspace), then the attention over them on the scores the
+  // indexer left in its workspace (V rows only)
   a.indices = indices ? indices : sel_pos;
+  a.keep_scores = true;
   a.out = out;
   a.lse = lse;
   hipError_t e = cs::launch_topk(a, hs);

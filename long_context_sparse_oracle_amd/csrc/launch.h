@@ -12,6 +12,10 @@ namespace cs {
 constexpr int kSparseWaveEntries = 16;
 constexpr int kSparseWaves = 8;
 
+// Positions sampled per (request, KV head) to set the candidate threshold of the filtered indexer;
+// caches of at most this many positions are scored whole and selected in one kernel.
+constexpr int kTauSamples = 1024;
+
 // int8 key sketch of the reduced-byte indexer: per key row, int8 codes in the K cache's layout
 // (element offset e of K holds code e) and one float32 scale (index e / D); the query rows'
 // codes and scales live in the indexer's workspace.
@@ -40,6 +44,10 @@ struct TopkLaunch {
   bool filtered;
   uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
   float* tau;         // [rows]: candidate thresholds
+  // max_len <= kTauSamples: one kernel scores every position and selects; keep_scores: it also
+  // writes every visible score to `scores` (the one-call step's attention reads them)
+  bool small;
+  bool keep_scores;
   // fused decode step (filtered path): selection and attention per row in one kernel
   bool fused;
   int32_t* sel_pos;   // [rows, k_max]

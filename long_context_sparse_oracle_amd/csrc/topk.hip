@@ -584,7 +584,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //     largest score is >= tau, so every position of the top-k is a candidate) and no slot
 //     overflowed; otherwise the workgroup recomputes every score of its row and selects from
 //     those (exact, slow, rare).
-constexpr int kTauSamples = 1024;
 constexpr int kCandFactor = 3;
 
 // Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
@@ -630,6 +629,52 @@ __device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int
     if (wave_sum_u32(c) >= (uint32_t)rr) P = cand;
   }
   return key_to_float(P << 16);
+}
+
+// The whole selection of one row whose every position has its key in krow (one wave; krow 16-byte
+// aligned, kTauSamples keys, 0 for a position not visible to the row, every visible key >= 1):
+// the kk largest keys (lower position first among equal keys) as ascending positions into out,
+// padded with -1 to k_max.  The kk-th largest key is found bit by bit with DPP wave sums.
+__device__ void row_select_all(const uint32_t* __restrict__ krow, int vis, int kk, int k_max,
+                               int32_t* __restrict__ out) {
+  constexpr int PER = kTauSamples / kWave;  // keys per lane: positions e * 64 + lane
+  const int lane = threadIdx.x & 63;
+  kk = kk < 0 ? 0 : (kk > vis ? vis : kk);
+  if (kk > 0 && kk < vis) {
+    uint32_t key[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) key[e] = krow[e * kWave + lane];
+    uint32_t P = 0;  // the largest P with at least kk keys >= P: the kk-th largest key
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = P | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) c += key[e] >= cand ? 1u : 0u;
+      if (wave_sum_u32(c) >= (uint32_t)kk) P = cand;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) gt += key[e] > P ? 1u : 0u;
+    const uint32_t need = (uint32_t)kk - wave_sum_u32(gt);  // keys equal to P that are taken
+    uint32_t eq_base = 0, out_base = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool is_eq = key[e] == P;
+      const uint64_t eqb = __ballot(is_eq);
+      const uint32_t eq_rank =
+          eq_base + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqb, 0u));
+      const bool sel = key[e] > P || (is_eq && eq_rank < need);
+      const uint64_t sb = __ballot(sel);
+      const uint32_t o =
+          out_base + __builtin_amdgcn_mbcnt_hi((uint32_t)(sb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sb, 0u));
+      if (sel) out[o] = e * kWave + lane;
+      eq_base += (uint32_t)__popcll(eqb);
+      out_base += (uint32_t)__popcll(sb);
+    }
+  } else {
+    for (int i = lane; i < kk; i += kWave) out[i] = i;  // none, or every visible position
+  }
+  for (int i = kk + lane; i < k_max; i += kWave) out[i] = -1;
 }
 
 // SK: this lane's A operand of query row qrow -- the 16 values j * 64 + g4 * 16 .. + 16 of each
@@ -686,10 +731,11 @@ __device__ __forceinline__ float quantize_q_operand(const uint16_t* __restrict__
 // largest of them; the workgroup also quantises its query rows and stores their codes and scales
 // for the later passes.
 constexpr int kSampleWaves = kTauSamples / 64;  // 16
-template <int D, bool PAGED, bool SK>
+template <int D, bool PAGED, bool SK, bool EXACT>
 __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
-    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ tau) {
+    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ tau,
+    int32_t* __restrict__ indices, float* __restrict__ scores, int64_t score_stride) {
   extern __shared__ uint32_t lkeys[];  // [16][kTauSamples]
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int kTiles = 4;                 // 16-sample tiles per wave
@@ -752,6 +798,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
   }
   int vis_i[4];
   float qsc[4];  // SK: scales of this lane's output rows
+  int64_t grow_i[4];  // EXACT: the rows' indices
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = 4 * g4 + i;
@@ -759,7 +806,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int t = r / G, gi = r - (r / G) * G;
     vis_i[i] = rl < rows_here ? L - T + t + 1 : 0;
     qsc[i] = SK ? __shfl(my_qsc, rl) : 0.f;  // lane rl holds row r0 + rl's scale
-    (void)gi;
+    grow_i[i] = ((int64_t)b * T + t) * Hq + (h * G + gi);
   }
 #pragma unroll
   for (int u = 0; u < kTiles; ++u) {
@@ -770,6 +817,9 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     for (int i = 0; i < 4; ++i) {
       const bool ok = j < ns && j * stride < vis_i[i];
       lkeys[(4 * g4 + i) * kTauSamples + j] = ok ? max(ord_key(sc[i]), 1u) : 0u;
+      if constexpr (EXACT) {  // every position is sampled (stride 1): keep the score for the step
+        if (ok && scores) scores[grow_i[i] * score_stride + j] = sc[i];
+      }
     }
   }
   __syncthreads();
@@ -780,8 +830,13 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int kb = k_req < 0 ? 0 : (k_req > k_max ? k_max : k_req);
     const int kk = min(kb, max(vis, 0));
     const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
-    const float th = row_tau(lkeys + wave * kTauSamples, vis, keep, stride);
-    if (lane == 0) tau[((int64_t)b * T + t) * Hq + (h * G + gi)] = th;
+    const int64_t grow = ((int64_t)b * T + t) * Hq + (h * G + gi);
+    if constexpr (EXACT) {
+      row_select_all(lkeys + wave * kTauSamples, max(vis, 0), kk, k_max, indices + grow * k_max);
+    } else {
+      const float th = row_tau(lkeys + wave * kTauSamples, vis, keep, stride);
+      if (lane == 0) tau[grow] = th;
+    }
   }
 }
 
@@ -1715,13 +1770,14 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     if ((e = launch_full_select_t<D, PAGED, true>(a, a.cand_mult, a.list_stride, a.list_pos, stream)) != hipSuccess)
       return e;
   } else {
-    auto samp = sample_tau_kernel<D, PAGED, SK>;
+    auto samp = sample_tau_kernel<D, PAGED, SK, false>;
     const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
     if ((e = hipFuncSetAttribute((const void*)samp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys)) !=
         hipSuccess)
       return e;
     hipLaunchKernelGGL(samp, dim3(groups, tiles), dim3(kSampleWaves * kWave), lds_keys, stream, a.q, a.kv, a.sk,
-                       a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, a.cand_mult, a.tau);
+                       a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, a.cand_mult, a.tau, nullptr, nullptr,
+                       (int64_t)0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
     const int rows_tile = a.GT < 16 ? a.GT : 16;
@@ -1786,8 +1842,26 @@ hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Caches of at most kTauSamples positions: the sample kernel scores every position, so it finishes
+// the selection itself (and, for the one-call step, keeps every score for the attention).
+template <int D, bool PAGED>
+static hipError_t launch_small_t(const TopkLaunch& a, hipStream_t stream) {
+  auto kern = sample_tau_kernel<D, PAGED, false, true>;
+  const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.kv.num_kv_heads, (a.GT + 15) / 16), dim3(kSampleWaves * kWave), lds_keys,
+                     stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, 1, a.tau, a.indices,
+                     a.keep_scores ? a.scores : nullptr, a.score_stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   if (a.sketch) return launch_filtered<true>(a, stream);
+  if (a.small) {
+    if (a.D == 128) return a.paged ? launch_small_t<128, true>(a, stream) : launch_small_t<128, false>(a, stream);
+    return a.paged ? launch_small_t<64, true>(a, stream) : launch_small_t<64, false>(a, stream);
+  }
   if (a.filtered) return launch_filtered<false>(a, stream);
   if (a.D == 128)
     return a.paged ? launch_full_select_t<128, true, false>(a, 1, a.k_max, a.indices, stream)

@@ -1,11 +1,11 @@
-"""GPU parity of the indexer's two paths against the CPU oracle.
+"""GPU parity of the indexer's paths against the CPU oracle.
 
 For k <= max_len / 16 the indexer first estimates a per-row score threshold from a strided sample
 of at most 1024 positions per (request, KV head), keeps only the positions scoring at or above it
 as candidates and selects among those; when fewer than k candidates survive (or a candidate slot
-overflows) the row is recomputed in full.  Larger k use the full-score path directly.  These
-tests drive each branch, the boundary between the paths and per-request k including 0 and
-k >= visible.
+overflows) the row is recomputed in full.  Larger k use the full-score path directly, and caches
+of at most 1024 positions are scored whole and selected in one kernel.  These tests drive each
+branch, the boundaries between the paths and per-request k including 0 and k >= visible.
 """
 
 import numpy as np
@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from tests._util import bits, oracle_cache
-from tests.gpu_util import all_rows, cache_of, check_topk_row
+from tests.gpu_util import all_rows, cache_of, check_attn_row, check_topk_row
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -103,3 +103,61 @@ def test_k_equals_max_len():
                        seq_lens=[512, 300], k=512, max_len=512, seed=47)
     idx = _check_indexer(wl)
     assert idx[0, 1, :, :512].tolist() == [list(range(512))] * 2
+
+
+# ---- caches of at most 1024 positions: every position is scored and selected in one kernel
+
+@pytest.mark.parametrize("max_len", [1024, 1025])
+def test_small_cache_boundary(max_len):
+    """1024 positions take the whole-row kernel, 1025 the regular paths: both exact, causal T = 4,
+    GQA 8 over two KV heads (two row tiles per KV head), paged and contiguous requests."""
+    for layout in ("contiguous", "paged"):
+        wl = make_workload(batch=2, q_len=4, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                           seq_lens=[max_len, 700], k=[40, 700], layout=layout, page_size=64, max_len=max_len,
+                           needles_per_head=2, seed=48)
+        idx = _check_indexer(wl, k_max=700)
+        # request 1 asks for more than it has: every visible position, ascending
+        for t in range(4):
+            assert idx[1, t, :, : 697 + t].tolist() == [list(range(697 + t))] * 16
+
+
+def test_small_cache_exact_ties_and_edges():
+    """All-equal keys (every score ties: the lowest positions win), a few strict winners mixed in,
+    k = 1, and k = 0 for one request, on a 1000-position cache, head_dim 64."""
+    m = _lib()
+    n = 1000
+    wl = make_workload(batch=2, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=64, seq_lens=[n, 600],
+                       k=[37, 0], max_len=n, seed=49)
+    wl.k_cache[0] = wl.k_cache[0, 0, 0]
+    wl.k_cache[0, 0, [5, n - 1, 321]] = (wl.q[0, 0, 3].float() * 4).to(torch.bfloat16)
+    g = wl.to("cuda")
+    idx = m.topk_index(g.q, cache_of(g), g.k_per_req, k_max=37).cpu().numpy()
+    idx1 = m.topk_index(g.q, cache_of(g), 1).cpu().numpy()
+    ocache = oracle_cache(wl)
+    q = oracle.bf16_bits_to_f64(bits(wl.q))
+    for hq in range(4):
+        np.testing.assert_array_equal(idx[0, 0, hq], oracle.row_topk(q[0, 0, hq], ocache.keys(0, 0), n, 37))
+        np.testing.assert_array_equal(idx1[0, 0, hq], oracle.row_topk(q[0, 0, hq], ocache.keys(0, 0), n, 1))
+        assert (idx[1, 0, hq] == -1).all()
+
+
+def test_small_cache_step_matches_oracle():
+    """The one-call step on a short cache (whole-row selection, then attention on the kept
+    scores): its lists by the band rule, its outputs against the oracle over those lists."""
+    m = _lib()
+    wl = make_workload(batch=3, q_len=2, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[900, 513, 64],
+                       k=[50, 20, 64], layout="paged", page_size=16, max_len=912, needles_per_head=1, seed=50)
+    g = wl.to("cuda")
+    o, l, idx = m.sparse_decode_step(g.q, cache_of(g), g.k_per_req, k_max=64, return_indices=True)
+    torch.cuda.synchronize()
+    o, l, idx = o.cpu().numpy(), l.cpu().numpy(), idx.cpu().numpy()
+    ocache = oracle_cache(wl)
+    q = oracle.bf16_bits_to_f64(bits(wl.q))
+    kreq = wl.k_per_req.numpy()
+    for b, t, hq in all_rows(wl):
+        K = ocache.keys(b, hq // wl.group)
+        V = ocache.values(b, hq // wl.group)
+        vis = oracle.visible_length(ocache.seq_lens[b], wl.q_len, t)
+        check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, min(int(kreq[b]), 64), f"row {(b, t, hq)}")
+        want = oracle.row_sparse(q[b, t, hq], K, V, idx[b, t, hq], vis)
+        check_attn_row(o[b, t, hq], l[b, t, hq], want[0], want[1], f"step row {(b, t, hq)}")
