@@ -29,6 +29,7 @@ around one call still counts about 4 µs of dispatch latency on top of the kerne
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -430,11 +431,16 @@ def main():
 
     all_evs = []
     torch.cuda.synchronize()
+    # no garbage collection while calls are queued: a collector pause between an event record and
+    # the launch after it would leave the GPU idle inside the timed window
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for k in range(args.steps):
         all_evs.extend(step(True, k))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     for name, e0, e1 in all_evs:
         times[name].append(hev.elapsed_us(e0, e1))
     for e0, e1 in pool:
