@@ -730,6 +730,9 @@ __device__ __forceinline__ float quantize_q_operand(const uint16_t* __restrict__
 // SK: sketch scores (int8 codes of q and K), and tau for the row's min(cand_mult * k', visible)
 // largest of them; the workgroup also quantises its query rows and stores their codes and scales
 // for the later passes.
+// EXACT (every request at most kTauSamples long, so stride 1 and the sample is the whole row):
+// wave w selects row w's top-k from the keys itself (row_select_all) into `indices` instead of
+// setting tau, and with `scores` keeps every visible score at scores[row * score_stride + n].
 constexpr int kSampleWaves = kTauSamples / 64;  // 16
 template <int D, bool PAGED, bool SK, bool EXACT>
 __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
