@@ -44,7 +44,8 @@ __device__ __forceinline__ void store_result(float O, float M, float Lsum, int c
 // one XCD (workgroup w runs on XCD w % 8, so group g gets the ids congruent to g mod 8): rows of
 // a GQA group that pick the same token find its K/V lines in that XCD's L2.
 // Indices are loaded one round ahead with one coalesced load and handed to the lanes with
-// ds_bpermute; a round then issues all of its K loads and then all of its V loads before using
+// ds_bpermute (paged caches: the entries two rounds ahead and their page ids one round ahead, so
+// no round's gathers wait on a page-table lookup); a round then issues all of its K loads and then all of its V loads before using
 // any: D/8 lanes hold one position (8 dims = 16 bytes of K and of V), 64/(D/8) positions per
 // step.  Scores are reduced across the D/8 lanes with DPP, the round's softmax statistics are
 // merged into the running (m, l, o); at the end the wave's position groups are merged with lane
@@ -108,38 +109,15 @@ sparse_partial_kernel(
   // split (k_max >= 1 makes hi - 1 a valid entry): the compiler then counts them like the
   // gathers and never has to drain the memory counter at the loop head.
   const int round_step = nwaves * E;
-  int base = lo + wave * E;
-  int next_idx = irow[min(base + lane, hi - 1)];
-  for (; base < hi; base += round_step) {
-    const int mine = base + lane < hi ? next_idx : -1;
-    next_idx = irow[min(base + round_step + lane, hi - 1)];
-    // a round of padding (-1) or otherwise invalid entries issues no loads
-    if (__ballot(mine >= 0 && mine < vis) == 0ull) continue;
-    int idx[NSTEP];
-#pragma unroll
-    for (int u = 0; u < NSTEP; ++u) idx[u] = __shfl(mine, u * PPW + p);
-    // Branch-free addresses: an entry outside [0, vis) reads position 0 (always present) and is
-    // masked out of the softmax below.
-    uint32_t okm = 0;
-    int64_t off[NSTEP];
-#pragma unroll
-    for (int u = 0; u < NSTEP; ++u) {
-      const bool ok = idx[u] >= 0 && idx[u] < vis;
-      okm |= (uint32_t)ok << u;
-      const int n = ok ? idx[u] : 0;
-      if constexpr (PAGED)
-        off[u] = kv_row<D, true>(kv, b, h, n) + c * 8;
-      else
-        off[u] = (int64_t)n * D + c * 8;
-    }
-    // every K load before any V load: the scores and their max can be formed while V arrives
+  // One round: the K/V rows at element offsets off[u] (entry u valid when bit u of okm is set),
+  // all K loads then all V loads in flight before any is used, then the online-softmax update.
+  auto gather_round = [&](const int64_t (&off)[NSTEP], uint32_t okm) __attribute__((always_inline)) {
     uint4 kr[NSTEP], vr[NSTEP];
 #pragma unroll
     for (int u = 0; u < NSTEP; ++u) kr[u] = ld16(kbase + off[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NSTEP; ++u) vr[u] = ld16(vbase + off[u]);
-    // keep the scheduler from pulling score math (and its waits) in between the loads
     __builtin_amdgcn_sched_barrier(0);
     float sv[NSTEP];
     float mx = -INFINITY;
@@ -155,7 +133,7 @@ sparse_partial_kernel(
       mx = fmaxf(mx, sv[u]);
     }
     const float m_new = fmaxf(m, mx);
-    if (m_new == -INFINITY) continue;
+    if (m_new == -INFINITY) return;
     const float alpha = fast_exp2(m - m_new);
     l *= alpha;
 #pragma unroll
@@ -170,6 +148,70 @@ sparse_partial_kernel(
       for (int i = 0; i < 8; ++i) o[i] = fmaf(pw, vf[i], o[i]);
     }
     m = m_new;
+  };
+  if constexpr (PAGED) {
+    // The page ids of a round's positions are loaded one round ahead (the entries two rounds
+    // ahead), so a round's K/V loads wait on no page-table lookup.  An invalid entry reads
+    // position 0's page and is masked out.
+    const int64_t pt_row = (int64_t)b * kv.max_pages;
+    auto pages_of = [&](int entry, int (&pg)[NSTEP]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NSTEP; ++u) {
+        const int x = __shfl(entry, u * PPW + p);
+        const int n = (x >= 0 && x < vis) ? x : 0;
+        pg[u] = kv.page_table[pt_row + (n >> kv.page_shift)];
+      }
+    };
+    int base = lo + wave * E;
+    int mine = base + lane < hi ? irow[min(base + lane, hi - 1)] : -1;
+    int pgc[NSTEP];
+    pages_of(mine, pgc);
+    int next_idx = irow[min(base + round_step + lane, hi - 1)];
+    for (; base < hi; base += round_step) {
+      const int nmine = base + round_step + lane < hi ? next_idx : -1;
+      next_idx = irow[min(base + 2 * round_step + lane, hi - 1)];
+      int pgn[NSTEP];
+      pages_of(nmine, pgn);
+      // a round of padding (-1) or otherwise invalid entries issues no loads
+      if (__ballot(mine >= 0 && mine < vis) != 0ull) {
+        uint32_t okm = 0;
+        int64_t off[NSTEP];
+#pragma unroll
+        for (int u = 0; u < NSTEP; ++u) {
+          const int x = __shfl(mine, u * PPW + p);
+          const bool ok = x >= 0 && x < vis;
+          okm |= (uint32_t)ok << u;
+          const int n = ok ? x : 0;
+          int page = pgc[u];
+          page = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
+          off[u] = ((((int64_t)page * kv.num_kv_heads + h) << kv.page_shift) + (n & ((1 << kv.page_shift) - 1))) * D +
+                   c * 8;
+        }
+        gather_round(off, okm);
+      }
+      mine = nmine;
+#pragma unroll
+      for (int u = 0; u < NSTEP; ++u) pgc[u] = pgn[u];
+    }
+  } else {
+    int base = lo + wave * E;
+    int next_idx = irow[min(base + lane, hi - 1)];
+    for (; base < hi; base += round_step) {
+      const int mine = base + lane < hi ? next_idx : -1;
+      next_idx = irow[min(base + round_step + lane, hi - 1)];
+      // a round of padding (-1) or otherwise invalid entries issues no loads
+      if (__ballot(mine >= 0 && mine < vis) == 0ull) continue;
+      uint32_t okm = 0;
+      int64_t off[NSTEP];
+#pragma unroll
+      for (int u = 0; u < NSTEP; ++u) {
+        const int x = __shfl(mine, u * PPW + p);
+        const bool ok = x >= 0 && x < vis;
+        okm |= (uint32_t)ok << u;
+        off[u] = (int64_t)(ok ? x : 0) * D + c * 8;
+      }
+      gather_round(off, okm);
+    }
   }
 
   // merge the wave's PPW position groups (lanes c + LPP p) with lane shuffles, then the waves
