@@ -194,7 +194,9 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
   SketchWs w;
   w.scores = 0;
   w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
-  w.counts = w.hist + (sketch_full(s, kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t)) : 0);
+  // histograms of the full-score mode, else the sample key prefixes of a split sample pass
+  w.counts = w.hist + (sketch_full(s, kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t))
+                                                            : align_up(rows * cs::kTauSamples * sizeof(uint16_t)));
   w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.q_codes = w.tau + align_up(rows * sizeof(float));
   w.q_scales = w.q_codes + align_up(rows * (size_t)s->head_dim);
@@ -342,6 +344,7 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.tau = reinterpret_cast<float*>(ws + lay.tau);
+  a.tau_prefixes = reinterpret_cast<uint16_t*>(ws + lay.hist);  // the histograms' area (unused by that path)
   a.indices = indices;
   return a;
 }
@@ -427,6 +430,7 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
   a.tau = reinterpret_cast<float*>(ws + lay.tau);
+  a.tau_prefixes = reinterpret_cast<uint16_t*>(ws + lay.hist);
   a.list_pos = reinterpret_cast<int32_t*>(ws + lay.list_pos);
   a.list_score = reinterpret_cast<float*>(ws + lay.list_score);
   a.list_stride = (int)sketch_list_stride(kv, k_max, cand_mult);

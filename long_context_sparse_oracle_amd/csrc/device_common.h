@@ -103,6 +103,14 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight stay in flight across
+// it (a full __syncthreads waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // a.lo * b.lo + a.hi * b.hi + c for two packed bf16 pairs (v_dot2_f32_bf16; the bf16 products

@@ -44,6 +44,7 @@ struct TopkLaunch {
   bool filtered;
   uint32_t* counts;   // [rows, cand_chunks, 4]: candidates per workgroup wave
   float* tau;         // [rows]: candidate thresholds
+  uint16_t* tau_prefixes;  // [rows, kTauSamples]: sample key prefixes of a split sample pass
   // max_len <= kTauSamples: one kernel scores every position and selects; keep_scores: it also
   // writes every visible score to `scores` (the one-call step's attention reads them)
   bool small;

@@ -604,31 +604,88 @@ __host__ __device__ constexpr int cand_cap(int chunk) { return chunk / (2 * kCan
 // relative spread about 1 / sqrt(r); kMinRank keeps that spread small for very sparse k (where
 // the kCandFactor rule alone would put r at a handful of samples).
 constexpr int kMinRank = 32;
-__device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int stride) {
-  const int lane = threadIdx.x & 63;
-  if (kk <= 0 || kk >= vis) return INFINITY;
+
+// The search for P on the 16-bit key prefixes of NR rows' samples, 16 per lane and row in any
+// order (0 for a sample the row does not see), for ranks rr; the rows' searches are interleaved
+// so that their wave sums overlap.
+template <int NR>
+__device__ void search_prefixes(const uint32_t (&k16)[NR][kTauSamples / kWave], const int (&rr)[NR],
+                                uint32_t (&P)[NR]) {
+#pragma unroll
+  for (int x = 0; x < NR; ++x) P[x] = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    uint32_t c[NR];
+#pragma unroll
+    for (int x = 0; x < NR; ++x) {
+      const uint32_t cand = P[x] | (1u << bit);
+      c[x] = 0;
+#pragma unroll
+      for (int e = 0; e < kTauSamples / kWave; ++e) c[x] += k16[x][e] >= cand ? 1u : 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < NR; ++x) c[x] = wave_sum_u32(c[x]);
+#pragma unroll
+    for (int x = 0; x < NR; ++x)
+      if (c[x] >= (uint32_t)rr[x]) P[x] |= 1u << bit;
+  }
+}
+
+// The rank r of a row's threshold, or 0 when the row needs no rank search (tau = *special).
+__device__ __forceinline__ int tau_rank(int vis, int kk, int stride, float* special) {
+  if (kk <= 0 || kk >= vis) {
+    *special = INFINITY;
+    return 0;
+  }
   const int ns_row = (vis + stride - 1) / stride;
   int64_t rr = ((int64_t)kCandFactor * kk * ns_row + vis - 1) / vis;
   if (rr < kMinRank) rr = kMinRank;
-  if (rr >= ns_row) return -INFINITY;
-  uint32_t k16[kTauSamples / kWave];
+  if (rr >= ns_row) {
+    *special = -INFINITY;
+    return 0;
+  }
+  return (int)rr;
+}
+
+// tau of a row whose sample keys (32-bit, kTauSamples of them) lie in LDS.
+__device__ float row_tau(const uint32_t* __restrict__ krow, int vis, int kk, int stride) {
+  const int lane = threadIdx.x & 63;
+  float special;
+  const int rr = tau_rank(vis, kk, stride, &special);
+  if (rr == 0) return special;
+  uint32_t k16[1][kTauSamples / kWave];
 #pragma unroll
   for (int e = 0; e < kTauSamples / kWave / 4; ++e) {
     const uint4 v = reinterpret_cast<const uint4*>(krow)[e * kWave + lane];
-    k16[4 * e] = v.x >> 16;
-    k16[4 * e + 1] = v.y >> 16;
-    k16[4 * e + 2] = v.z >> 16;
-    k16[4 * e + 3] = v.w >> 16;
+    k16[0][4 * e] = v.x >> 16;
+    k16[0][4 * e + 1] = v.y >> 16;
+    k16[0][4 * e + 2] = v.z >> 16;
+    k16[0][4 * e + 3] = v.w >> 16;
   }
-  uint32_t P = 0;
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t cand = P | (1u << bit);
-    uint32_t c = 0;
+  const int rrs[1] = {rr};
+  uint32_t P[1];
+  search_prefixes<1>(k16, rrs, P);
+  return key_to_float(P[0] << 16);
+}
+
+// A lane's share of a row's sample key prefixes (16-bit, kTauSamples of them, 16-byte aligned) as
+// a split sample pass leaves them in global memory: 16 prefixes in two 16-byte words.
+__device__ __forceinline__ void load_prefixes(const uint16_t* __restrict__ krow, uint4 (&w)[2]) {
+  const int lane = threadIdx.x & 63;
+  w[0] = reinterpret_cast<const uint4*>(krow)[lane];
+  w[1] = reinterpret_cast<const uint4*>(krow)[kWave + lane];
+}
+
+// The 16 prefixes of two words from load_prefixes, one per entry.
+__device__ __forceinline__ void unpack_prefixes(const uint4 (&pw)[2], uint32_t (&k16)[kTauSamples / kWave]) {
 #pragma unroll
-    for (int e = 0; e < kTauSamples / kWave; ++e) c += k16[e] >= cand ? 1u : 0u;
-    if (wave_sum_u32(c) >= (uint32_t)rr) P = cand;
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t w[4] = {pw[e].x, pw[e].y, pw[e].z, pw[e].w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      k16[8 * e + 2 * x] = w[x] & 0xffffu;
+      k16[8 * e + 2 * x + 1] = w[x] >> 16;
+    }
   }
-  return key_to_float(P << 16);
 }
 
 // The whole selection of one row whose every position has its key in krow (one wave; krow 16-byte
@@ -733,15 +790,22 @@ __device__ __forceinline__ float quantize_q_operand(const uint16_t* __restrict__
 // EXACT (every request at most kTauSamples long, so stride 1 and the sample is the whole row):
 // wave w selects row w's top-k from the keys itself (row_select_all) into `indices` instead of
 // setting tau, and with `scores` keeps every visible score at scores[row * score_stride + n].
+// SPLIT > 1: SPLIT workgroups (blockIdx.z) share a tile's samples, a quarter or half each, and
+// store the samples' 16-bit key prefixes at prefixes[row * kTauSamples + j] instead of setting tau;
+// the candidate pass then sets tau from them.  A sample pass is bound by the sampled rows one
+// compute unit has in flight, so spreading a tile over several units shortens it when there are
+// fewer tiles than units.
 constexpr int kSampleWaves = kTauSamples / 64;  // 16
-template <int D, bool PAGED, bool SK, bool EXACT>
+template <int D, bool PAGED, bool SK, bool EXACT, int SPLIT>
 __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
     const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ tau,
-    int32_t* __restrict__ indices, float* __restrict__ scores, int64_t score_stride) {
-  extern __shared__ uint32_t lkeys[];  // [16][kTauSamples]
+    int32_t* __restrict__ indices, float* __restrict__ scores, int64_t score_stride,
+    uint16_t* __restrict__ prefixes) {
+  static_assert(SPLIT == 1 || (!EXACT && (SPLIT == 2 || SPLIT == 4)), "split sampling sets no selection");
+  extern __shared__ uint32_t lkeys[];  // [16][kTauSamples] (SPLIT == 1)
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
-  constexpr int kTiles = 4;                 // 16-sample tiles per wave
+  constexpr int kTiles = 4 / SPLIT;         // 16-sample tiles per wave
   const int bh = blockIdx.x;
   const int mt = blockIdx.y;
   const int Hkv = kv.num_kv_heads;
@@ -767,7 +831,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int64_t qr = ((int64_t)b * T + t) * Hq + (h * G + gi);
     if constexpr (SK) {
       my_qsc = quantize_q_operand<D>(q + (r < GT ? qr : 0) * D, r < GT, g4, a);
-      if (r < GT && wave == 0) {
+      if (r < GT && wave == 0 && blockIdx.z == 0) {
 #pragma unroll
         for (int j = 0; j < KS; ++j) *reinterpret_cast<uint4*>(sk.q_codes + qr * D + g4 * 16 + j * 64) = a[j];
         if (g4 == 0) sk.q_scales[qr] = my_qsc;
@@ -780,7 +844,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
       for (int j = 0; j < KS; ++j) a[j] = make_uint4(0, 0, 0, 0);
     }
   }
-  const int j0 = 64 * wave;
+  const int j0 = (int)blockIdx.z * (kTauSamples / SPLIT) + 16 * kTiles * wave;
   uint4 kt[kTiles][KS];
   float ksc[kTiles];  // SK: the sampled rows' scales
   const int jlast = max(ns - 1, 0);
@@ -819,12 +883,18 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = j < ns && j * stride < vis_i[i];
-      lkeys[(4 * g4 + i) * kTauSamples + j] = ok ? max(ord_key(sc[i]), 1u) : 0u;
+      const uint32_t key = ok ? max(ord_key(sc[i]), 1u) : 0u;
+      if constexpr (SPLIT == 1) {
+        lkeys[(4 * g4 + i) * kTauSamples + j] = key;
+      } else if (4 * g4 + i < rows_here) {
+        prefixes[grow_i[i] * kTauSamples + j] = (uint16_t)(key >> 16);
+      }
       if constexpr (EXACT) {  // every position is sampled (stride 1): keep the score for the step
         if (ok && scores) scores[grow_i[i] * score_stride + j] = sc[i];
       }
     }
   }
+  if constexpr (SPLIT > 1) return;
   __syncthreads();
   if (wave < rows_here) {
     const int r = r0 + wave;
@@ -849,13 +919,17 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
 //
 // SK (reduced-byte indexer): positions are scored on the sketch, and each row keeps the
 // candidates for its min(cand_mult * k, visible) largest sketch scores.
-template <int D, bool PAGED, int NI, bool SK>
+// PREFIX (after a split sample pass): the workgroup sets its rows' thresholds itself from the
+// sample key prefixes, wave w those of rows w, w + 4, ..., instead of reading tau.
+template <int D, bool PAGED, int NI, bool SK, bool PREFIX>
 __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     const uint16_t* __restrict__ q, KVArgs kv, SketchArgs sk, int T, int Hq, int G, float scale,
-    const float* __restrict__ tau, float* __restrict__ region, int64_t score_stride,
-    uint32_t* __restrict__ counts, int chunk, int chunks) {
+    const float* __restrict__ tau, const uint16_t* __restrict__ prefixes,
+    const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ region,
+    int64_t score_stride, uint32_t* __restrict__ counts, int chunk, int chunks) {
   extern __shared__ int lds_pages[];
   __shared__ __align__(16) uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
+  __shared__ float tau_sh[16];                                 // PREFIX: the tile's thresholds
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int UNR = kScoreUnroll;  // tiles per step (twice as many for the sketch measured no faster)
   const int c = blockIdx.x;
@@ -897,6 +971,66 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     }
   }
   __syncthreads();  // page ids
+  // UNR adjacent 16-position tiles per iteration; the next iteration's K loads while this one
+  // is scored (ping-pong, unconditional loads clamped to the range's last tile; a wave with no
+  // range loads the chunk's first tile)
+  constexpr int kStep = 16 * UNR;
+  const int last = wend > wbeg ? (wend - 1) & ~15 : (PREFIX ? start : wbeg);
+  uint4 cur[UNR][KS], nxt[UNR][KS];
+  float csc[UNR], nsc[UNR];  // SK: the tiles' key scales (this lane's position)
+  auto load_tiles = [&](int n0, uint4 (&dst)[UNR][KS], float (&dsc)[UNR]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int tile = min(n0 + u * 16, last);
+      const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
+                          (int64_t)min(m, L - 1 - tile) * D;
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        dst[u][j] = SK ? ld16i8(sk.codes + off + g4 * 16 + j * 64) : ld16(kv.k + off + g4 * 8 + j * 32);
+      dsc[u] = SK ? sk.scales[off / D] : 0.f;
+    }
+  };
+  // PREFIX: wave w sets the thresholds of rows w + 4 x (x < NI, as rows <= 4 NI).  Their
+  // prefixes load first, then the first tiles (every wave, unconditionally: a wave with no range
+  // loads the chunk's first tile, so no branch precedes the loop), and the searches run while
+  // the tiles are in flight.
+  if constexpr (PREFIX) {
+    uint4 pref[NI][2];
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const int r = r0 + wave + kCandWaves * x;
+      const int t = r / G, gi = r - (r / G) * G;
+      if (wave + kCandWaves * x < rows_here) {
+        load_prefixes(prefixes + (((int64_t)b * T + t) * Hq + (h * G + gi)) * kTauSamples, pref[x]);
+      } else {
+        pref[x][0] = pref[x][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    load_tiles(wbeg, cur, csc);
+    const int k_req = k_per_req ? k_per_req[b] : k_max;
+    const int kb = k_req < 0 ? 0 : (k_req > k_max ? k_max : k_req);
+    const int stride = tau_stride(L);
+    int rr[NI];
+    float special[NI];
+    uint32_t k16[NI][kTauSamples / kWave];
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const int t = (r0 + wave + kCandWaves * x) / G;
+      const int vis = L - T + t + 1;
+      const int kk = min(kb, max(vis, 0));
+      const int keep = SK ? (int)min((int64_t)cand_mult * kk, (int64_t)max(vis, 0)) : kk;
+      rr[x] = tau_rank(vis, keep, stride, &special[x]);
+      unpack_prefixes(pref[x], k16[x]);
+    }
+    uint32_t P[NI];
+    search_prefixes<NI>(k16, rr, P);
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const int rl = wave + kCandWaves * x;
+      if (rl < rows_here && lane == 0) tau_sh[rl] = rr[x] ? key_to_float(P[x] << 16) : special[x];
+    }
+    lds_barrier();
+  }
   // Candidate lines are written with buffer stores through one resource spanning this
   // workgroup's rows; a lane with nothing to write passes an offset past the resource, which
   // the hardware drops.  Every tile thus issues the same stores with no branch around them, and
@@ -936,7 +1070,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       const int t = r / G, gi = r - (r / G) * G;
       grow[i] = ((int64_t)b * T + t) * Hq + (h * G + gi);
       vis[i] = L - T + t + 1;
-      th[i] = tau[grow[i]];
+      th[i] = PREFIX ? tau_sh[rl] : tau[grow[i]];
       qsc[i] = SK ? sk.q_scales[grow[i]] : 0.f;
     } else {
       grow[i] = 0;
@@ -948,24 +1082,6 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
                          (int64_t)(c * kCandWaves + wave) * 128);
   }
 
-  // UNR adjacent 16-position tiles per iteration; the next iteration's K loads while this one
-  // is scored (ping-pong, unconditional loads clamped to the range's last tile)
-  constexpr int kStep = 16 * UNR;
-  const int last = wend > wbeg ? (wend - 1) & ~15 : wbeg;
-  uint4 cur[UNR][KS], nxt[UNR][KS];
-  float csc[UNR], nsc[UNR];  // SK: the tiles' key scales (this lane's position)
-  auto load_tiles = [&](int n0, uint4 (&dst)[UNR][KS], float (&dsc)[UNR]) {
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int tile = min(n0 + u * 16, last);
-      const int64_t off = kv_tile_staged<D, PAGED>(kv, lds_pages, start, b, h, tile) +
-                          (int64_t)min(m, L - 1 - tile) * D;
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        dst[u][j] = SK ? ld16i8(sk.codes + off + g4 * 16 + j * 64) : ld16(kv.k + off + g4 * 8 + j * 32);
-      dsc[u] = SK ? sk.scales[off / D] : 0.f;
-    }
-  };
   // Per tile and row: candidates s >= tau join the row's 32-entry LDS ring; once it holds 16, the
   // 16 from its head are written as one 128-byte line.
   // Tiles past the range (the second of a pair at the end) are scored on reloaded data and
@@ -1026,7 +1142,7 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
   };
   if (wbeg < wend) {
     int n0 = wbeg;
-    load_tiles(n0, cur, csc);
+    if constexpr (!PREFIX) load_tiles(n0, cur, csc);
     do {
       load_tiles(n0 + kStep, nxt, nsc);
       score_tiles(n0, cur, csc);
@@ -1773,22 +1889,38 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
     if ((e = launch_full_select_t<D, PAGED, true>(a, a.cand_mult, a.list_stride, a.list_pos, stream)) != hipSuccess)
       return e;
   } else {
-    auto samp = sample_tau_kernel<D, PAGED, SK, false>;
-    const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
-    if ((e = hipFuncSetAttribute((const void*)samp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys)) !=
-        hipSuccess)
-      return e;
-    hipLaunchKernelGGL(samp, dim3(groups, tiles), dim3(kSampleWaves * kWave), lds_keys, stream, a.q, a.kv, a.sk,
-                       a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, a.cand_mult, a.tau, nullptr, nullptr,
-                       (int64_t)0);
+    // At most half as many tiles as compute units: four workgroups per tile sample, and every
+    // candidate workgroup sets its rows' thresholds.  Measured: the sample pass drops from 15-16
+    // to 7-8 us, the candidate pass grows by 1-3 us; on the sketch, whose candidate workgroups
+    // are short, with 8 rows per tile the growth exceeds the saving.
+    const int rows_tile = a.GT < 16 ? a.GT : 16;
+    const bool split = 2 * groups * tiles <= a.cus && (!SK || rows_tile <= 4);
+    if (split) {
+      hipLaunchKernelGGL((sample_tau_kernel<D, PAGED, SK, false, 4>), dim3(groups, tiles, 4),
+                         dim3(kSampleWaves * kWave), 0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale,
+                         a.k_per_req, a.k_max, a.cand_mult, a.tau, nullptr, nullptr, (int64_t)0, a.tau_prefixes);
+    } else {
+      auto samp = sample_tau_kernel<D, PAGED, SK, false, 1>;
+      const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
+      if ((e = hipFuncSetAttribute((const void*)samp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys)) !=
+          hipSuccess)
+        return e;
+      hipLaunchKernelGGL(samp, dim3(groups, tiles), dim3(kSampleWaves * kWave), lds_keys, stream, a.q, a.kv, a.sk,
+                         a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, a.cand_mult, a.tau, nullptr, nullptr,
+                         (int64_t)0, nullptr);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t page_ids = PAGED ? (size_t)(a.cand_chunk >> a.kv.page_shift) + 2 : 0;
-    const int rows_tile = a.GT < 16 ? a.GT : 16;
-    auto cand = rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK>
-                               : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK> : score_cand_kernel<D, PAGED, 4, SK>);
+    auto cand = split ? (rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK, true>
+                                        : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK, true>
+                                                          : score_cand_kernel<D, PAGED, 4, SK, true>))
+                      : (rows_tile <= 4 ? score_cand_kernel<D, PAGED, 1, SK, false>
+                                        : (rows_tile <= 8 ? score_cand_kernel<D, PAGED, 2, SK, false>
+                                                          : score_cand_kernel<D, PAGED, 4, SK, false>));
     hipLaunchKernelGGL(cand, dim3(a.cand_chunks, groups, tiles), dim3(kCandWaves * kWave),
                        page_ids * sizeof(int), stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.tau,
-                       a.scores, a.score_stride, a.counts, a.cand_chunk, a.cand_chunks);
+                       a.tau_prefixes, a.k_per_req, a.k_max, a.cand_mult, a.scores,
+                       a.score_stride, a.counts, a.cand_chunk, a.cand_chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
@@ -1849,13 +1981,13 @@ hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream) {
 // the selection itself (and, for the one-call step, keeps every score for the attention).
 template <int D, bool PAGED>
 static hipError_t launch_small_t(const TopkLaunch& a, hipStream_t stream) {
-  auto kern = sample_tau_kernel<D, PAGED, false, true>;
+  auto kern = sample_tau_kernel<D, PAGED, false, true, 1>;
   const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.B * a.kv.num_kv_heads, (a.GT + 15) / 16), dim3(kSampleWaves * kWave), lds_keys,
                      stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req, a.k_max, 1, a.tau, a.indices,
-                     a.keep_scores ? a.scores : nullptr, a.score_stride);
+                     a.keep_scores ? a.scores : nullptr, a.score_stride, nullptr);
   return hipGetLastError();
 }
 

@@ -161,3 +161,29 @@ def test_small_cache_step_matches_oracle():
         check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, min(int(kreq[b]), 64), f"row {(b, t, hq)}")
         want = oracle.row_sparse(q[b, t, hq], K, V, idx[b, t, hq], vis)
         check_attn_row(o[b, t, hq], l[b, t, hq], want[0], want[1], f"step row {(b, t, hq)}")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_sample_pass_one_workgroup_per_tile(layout):
+    """With at least half as many (request, KV head, 16-row tile) groups as compute units, one
+    workgroup samples each tile and sets its thresholds; with fewer (the other tests here), four
+    workgroups share a tile's samples and the candidate pass sets the thresholds.  160 groups,
+    ragged lengths, q_len 2; the indexer and the one-call step's lists."""
+    m = _lib()
+    rng = np.random.default_rng(51)
+    lens = rng.integers(1100, 2049, size=40).tolist()
+    wl = make_workload(batch=40, q_len=2, num_q_heads=8, num_kv_heads=4, head_dim=64, seq_lens=lens,
+                       k=0.05, layout=layout, page_size=16, max_len=2048, needles_per_head=1, seed=51)
+    assert int(wl.k_per_req.max()) <= 2048 // 16  # the candidate path
+    _check_indexer(wl)
+    g = wl.to("cuda")
+    o, l, idx = m.sparse_decode_step(g.q, cache_of(g), g.k_per_req, k_max=wl.k_max, return_indices=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    ocache = oracle_cache(wl)
+    q = oracle.bf16_bits_to_f64(bits(wl.q))
+    kreq = wl.k_per_req.numpy()
+    for b, t, hq in all_rows(wl):
+        vis = oracle.visible_length(ocache.seq_lens[b], wl.q_len, t)
+        check_topk_row(idx[b, t, hq], q[b, t, hq], ocache.keys(b, hq // wl.group), vis,
+                       min(int(kreq[b]), wl.k_max), f"step row {(b, t, hq)}")
