@@ -792,7 +792,8 @@ __device__ __forceinline__ float quantize_q_operand(const uint16_t* __restrict__
 // setting tau, and with `scores` keeps every visible score at scores[row * score_stride + n].
 // SPLIT > 1: SPLIT workgroups (blockIdx.z) share a tile's samples, a quarter or half each, and
 // store the samples' 16-bit key prefixes at prefixes[row * kTauSamples + j] instead of setting tau;
-// the candidate pass then sets tau from them.  A sample pass is bound by the sampled rows one
+// the candidate pass then sets tau from them.  With EXACT they store the whole 32-bit keys
+// (prefixes read as uint32_t) and small_select_kernel selects.  A sample pass is bound by the sampled rows one
 // compute unit has in flight, so spreading a tile over several units shortens it when there are
 // fewer tiles than units.
 constexpr int kSampleWaves = kTauSamples / 64;  // 16
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
     const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ tau,
     int32_t* __restrict__ indices, float* __restrict__ scores, int64_t score_stride,
     uint16_t* __restrict__ prefixes) {
-  static_assert(SPLIT == 1 || (!EXACT && (SPLIT == 2 || SPLIT == 4)), "split sampling sets no selection");
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "a tile's samples split into 1, 2 or 4 parts");
   extern __shared__ uint32_t lkeys[];  // [16][kTauSamples] (SPLIT == 1)
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int kTiles = 4 / SPLIT;         // 16-sample tiles per wave
@@ -887,7 +888,10 @@ __global__ __launch_bounds__(kSampleWaves * kWave) void sample_tau_kernel(
       if constexpr (SPLIT == 1) {
         lkeys[(4 * g4 + i) * kTauSamples + j] = key;
       } else if (4 * g4 + i < rows_here) {
-        prefixes[grow_i[i] * kTauSamples + j] = (uint16_t)(key >> 16);
+        if constexpr (EXACT)
+          reinterpret_cast<uint32_t*>(prefixes)[grow_i[i] * kTauSamples + j] = key;
+        else
+          prefixes[grow_i[i] * kTauSamples + j] = (uint16_t)(key >> 16);
       }
       if constexpr (EXACT) {  // every position is sampled (stride 1): keep the score for the step
         if (ok && scores) scores[grow_i[i] * score_stride + j] = sc[i];
@@ -1977,10 +1981,41 @@ hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Selection of caches of at most kTauSamples positions whose keys a split whole-row pass stored
+// (keys[row * kTauSamples + n], 0 for a position the row does not see): one wave per row.
+__global__ __launch_bounds__(4 * kWave) void small_select_kernel(KVArgs kv, int T, int Hq, int rows,
+                                                                 const int32_t* __restrict__ k_per_req, int k_max,
+                                                                 const uint32_t* __restrict__ keys,
+                                                                 int32_t* __restrict__ indices) {
+  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int b = row / (T * Hq);
+  const int t = row / Hq - b * T;
+  const int vis = max(seq_len_of(kv, b) - T + t + 1, 0);
+  const int k_req = k_per_req ? k_per_req[b] : k_max;
+  const int kb = k_req < 0 ? 0 : (k_req > k_max ? k_max : k_req);
+  row_select_all(keys + (int64_t)row * kTauSamples, vis, min(kb, vis), k_max, indices + (int64_t)row * k_max);
+}
+
 // Caches of at most kTauSamples positions: the sample kernel scores every position, so it finishes
-// the selection itself (and, for the one-call step, keeps every score for the attention).
+// the selection itself (and, for the one-call step, keeps every score for the attention).  With
+// at most half as many tiles as compute units, four workgroups per tile score a quarter of the
+// positions each and store the keys, and small_select_kernel selects: the scoring is bound by the
+// rows one compute unit has in flight, which one workgroup per tile leaves on a few units.
 template <int D, bool PAGED>
 static hipError_t launch_small_t(const TopkLaunch& a, hipStream_t stream) {
+  const int groups = a.B * a.kv.num_kv_heads, tiles = (a.GT + 15) / 16;
+  if (2 * groups * tiles <= a.cus) {
+    hipLaunchKernelGGL((sample_tau_kernel<D, PAGED, false, true, 4>), dim3(groups, tiles, 4),
+                       dim3(kSampleWaves * kWave), 0, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale,
+                       a.k_per_req, a.k_max, 1, a.tau, nullptr, a.keep_scores ? a.scores : nullptr,
+                       a.score_stride, a.tau_prefixes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(small_select_kernel, dim3((a.rows + 3) / 4), dim3(4 * kWave), 0, stream, a.kv, a.T, a.Hq,
+                       a.rows, a.k_per_req, a.k_max, reinterpret_cast<const uint32_t*>(a.tau_prefixes), a.indices);
+    return hipGetLastError();
+  }
   auto kern = sample_tau_kernel<D, PAGED, false, true, 1>;
   const size_t lds_keys = (size_t)16 * kTauSamples * sizeof(uint32_t);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_keys);

@@ -187,3 +187,31 @@ def test_sample_pass_one_workgroup_per_tile(layout):
         vis = oracle.visible_length(ocache.seq_lens[b], wl.q_len, t)
         check_topk_row(idx[b, t, hq], q[b, t, hq], ocache.keys(b, hq // wl.group), vis,
                        min(int(kreq[b]), wl.k_max), f"step row {(b, t, hq)}")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_small_cache_one_workgroup_per_tile(layout):
+    """Caches of at most 1024 positions with at least half as many tiles as compute units: one
+    workgroup per tile scores the whole row and selects (with fewer tiles, four workgroups score a
+    quarter each and a second kernel selects: the other small-cache tests).  160 groups, ragged
+    lengths, q_len 2; the indexer and the one-call step's lists and outputs."""
+    m = _lib()
+    rng = np.random.default_rng(52)
+    lens = rng.integers(300, 1001, size=40).tolist()
+    wl = make_workload(batch=40, q_len=2, num_q_heads=8, num_kv_heads=4, head_dim=64, seq_lens=lens,
+                       k=0.05, layout=layout, page_size=16, max_len=1008, needles_per_head=1, seed=52)
+    _check_indexer(wl)
+    g = wl.to("cuda")
+    o, l, idx = m.sparse_decode_step(g.q, cache_of(g), g.k_per_req, k_max=wl.k_max, return_indices=True)
+    torch.cuda.synchronize()
+    o, l, idx = o.cpu().numpy(), l.cpu().numpy(), idx.cpu().numpy()
+    ocache = oracle_cache(wl)
+    q = oracle.bf16_bits_to_f64(bits(wl.q))
+    kreq = wl.k_per_req.numpy()
+    for b, t, hq in all_rows(wl):
+        K = ocache.keys(b, hq // wl.group)
+        vis = oracle.visible_length(ocache.seq_lens[b], wl.q_len, t)
+        check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, min(int(kreq[b]), wl.k_max), f"step row {(b, t, hq)}")
+        if b % 8 == 0:
+            want = oracle.row_sparse(q[b, t, hq], K, ocache.values(b, hq // wl.group), idx[b, t, hq], vis)
+            check_attn_row(o[b, t, hq], l[b, t, hq], want[0], want[1], f"step row {(b, t, hq)}")
