@@ -133,9 +133,9 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
  * results as those two calls; `indices` (device int32 [B, T, Hq, k_max]) may be NULL when the
  * lists themselves are not wanted.  For k_max <= max_len / 16 (and max_len > 1024) each row's
  * selection and its attention run in one workgroup on the scores the indexer already computed;
- * otherwise the indexer (its full-score pass, or for max_len <= 1024 the one kernel that scores
- * and selects whole rows) leaves every score in the workspace and a second kernel attends over
- * each row's list on those scores.  Either way only the V rows of the selected positions are
+ * otherwise the indexer (its full-score pass, or for max_len <= 1024 the whole-row pass that
+ * scores every position and selects) leaves every score in the workspace and a further kernel
+ * attends over each row's list on those scores.  Either way only the V rows of the selected positions are
  * read for the attention.  out / lse agree with sparse_decode_attn over the exact top-k lists within the
  * same tolerances (the scores come from the indexer's float32 dot products).
  * Errors: as topk_index and sparse_decode_attn.
