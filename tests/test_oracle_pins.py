@@ -385,3 +385,91 @@ def test_golden_fixture_reproduced():
     # every needle is in its head's selection
     for b, t, hq, p in rec["needles"]:
         assert p in rec["topk_indices"][b][t][hq]
+
+
+# ----------------------------------------------------------------------------- decode_sparse
+def _gqa_ragged_paged(seed=21):
+    # GQA 8:2 (four query heads per KV head), three new tokens per request, ragged lengths,
+    # paged cache with a permuted page table
+    return make_workload(
+        batch=3, q_len=3, num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=[70, 33, 129],
+        k=9, layout="paged", page_size=16, max_len=144, needles_per_head=0, seed=seed,
+    )
+
+
+def test_decode_sparse_all_visible_equals_dense():
+    """Sparse attention over every visible position, listed shuffled and -1 padded, is dense
+    attention (the method's k = N case), row by row; a wrong KV-head map or a causal window that
+    ignores the token index gives a different row or an out-of-range entry."""
+    wl = _gqa_ragged_paged()
+    cache = oracle_cache(wl)
+    qb = bits(wl.q)
+    B, T, Hq = wl.batch, wl.q_len, wl.num_q_heads
+    lens = wl.seq_lens.tolist()
+    kpad = max(lens) + 5
+    idx = np.full((B, T, Hq, kpad), -1, dtype=np.int32)
+    rng = np.random.default_rng(7)
+    for b in range(B):
+        for t in range(T):
+            vis = lens[b] - T + t + 1  # token t of the T appended tokens sees 0 .. L - T + t
+            for hq in range(Hq):
+                slots = rng.permutation(kpad)[:vis]  # padding interleaved, not only at the end
+                idx[b, t, hq, slots] = rng.permutation(vis)
+    o_s, l_s = oracle.decode_sparse(qb, cache, idx)
+    o_d, l_d = oracle.decode_dense(qb, cache)
+    np.testing.assert_allclose(o_s, o_d, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_s, l_d, rtol=0, atol=1e-12)
+
+
+def test_decode_sparse_against_independent_page_walk():
+    """Sampled rows of `decode_sparse` against a row computed here without the oracle's cache
+    view, head map or causal window: K and V gathered by walking the page table with torch, the
+    KV head written out per query head, softmax by SciPy."""
+    wl = _gqa_ragged_paged(seed=22)
+    cache = oracle_cache(wl)
+    qb = bits(wl.q)
+    B, T, Hq, d = wl.batch, wl.q_len, wl.num_q_heads, wl.head_dim
+    lens = wl.seq_lens.tolist()
+    kv_head_of = [0, 0, 0, 0, 1, 1, 1, 1]  # Hq = 8 on Hkv = 2, contiguous groups of four
+    rng = np.random.default_rng(8)
+    kmax = 12
+    idx = np.full((B, T, Hq, kmax), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            last = lens[b] - T + t  # last position token t may see
+            for hq in range(Hq):
+                n = int(rng.integers(1, kmax + 1))
+                idx[b, t, hq, :n] = rng.integers(0, last + 1, size=n)  # repeats allowed
+                if t == T - 1:
+                    idx[b, t, hq, 0] = last  # the last token reaches the newest position
+    o, lse = oracle.decode_sparse(qb, cache, idx)
+    q = wl.q.double()
+    for b, t, hq in [(0, 0, 0), (0, 2, 7), (1, 1, 3), (1, 2, 4), (2, 0, 5), (2, 2, 1), (2, 1, 6)]:
+        h = kv_head_of[hq]
+        pos = [int(p) for p in idx[b, t, hq] if p != -1]
+        krows = torch.stack([wl.k_cache[int(wl.page_table[b, p // 16]), h, p % 16] for p in pos])
+        vrows = torch.stack([wl.v_cache[int(wl.page_table[b, p // 16]), h, p % 16] for p in pos])
+        s = (krows.double() @ q[b, t, hq]).numpy() / math.sqrt(d)
+        w = scipy.special.softmax(s)
+        np.testing.assert_allclose(o[b, t, hq], w @ vrows.double().numpy(), rtol=0, atol=1e-12)
+        assert abs(lse[b, t, hq] - scipy.special.logsumexp(s)) <= 1e-12
+
+
+def test_decode_sparse_rejects_positions_past_each_tokens_window():
+    """Token t of T sees positions 0 .. L - T + t: one entry past that window is an error for
+    every token, and the same entry is accepted by the next token."""
+    wl = _gqa_ragged_paged(seed=23)
+    cache = oracle_cache(wl)
+    qb = bits(wl.q)
+    B, T, Hq = wl.batch, wl.q_len, wl.num_q_heads
+    lens = wl.seq_lens.tolist()
+    for b in range(B):
+        for t in range(T):
+            idx = np.full((B, T, Hq, 2), -1, dtype=np.int32)
+            idx[b, t, 5, 0] = lens[b] - T + t + 1
+            with pytest.raises(ValueError):
+                oracle.decode_sparse(qb, cache, idx, rows=[(b, t, 5)])
+            if t + 1 < T:
+                idx2 = np.full((B, T, Hq, 2), -1, dtype=np.int32)
+                idx2[b, t + 1, 5, 0] = lens[b] - T + t + 1
+                oracle.decode_sparse(qb, cache, idx2, rows=[(b, t + 1, 5)])
