@@ -1,7 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark: one oracle-top-k sparse decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama3_8b_n32k_k655]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload ragged_paged_b32_t4]
+
+The default workload is the largest single-GPU setting: the agentic ragged paged batch (32
+requests, cached lengths uniform in [8192, 131072], 4 new tokens each, GQA 32/8, d = 128, pages of
+16 positions in a permuted page table, k_b = 2% of L_b per token and head).
 
 A step is one pass of the whole hot path over one decode batch, on one stream:
     flush -> topk_index -> flush -> sparse_decode_attn -> flush -> dense_decode_attn
@@ -15,13 +19,21 @@ KV bytes when a hot-path call starts (every call is measured from cold caches). 
 bracketed by HIP events recorded on the stream it runs on.  Inputs are seeded synthetic tensors
 drawn on the GPU before the timed region.
 
-Prints ONE JSON line.  `value` is the sparse decode attention's gathered-KV throughput: the
+Prints ONE JSON line.  `ms_per_step` is one pass of the hot path on the batch: the mean event
+times of topk_index + sparse_decode_attn + dense_decode_attn (the indexer, the sparse attention
+and the dense baseline; flushes and the other calls excluded; the wall time of a whole timed
+iteration is `wall_ms_per_iteration`).  `value` is the sparse decode attention's gathered-KV
+throughput: the
 distinct K/V rows the step's index lists name (counted once per (request, KV head) group, 512 B
 each at d=128) plus index, query and output bytes, divided by the mean duration of the
 sparse_decode_attn call.  Also reported: µs of every call (mean, and p10/p50/p90), speedup over
 the dense decode on the same inputs, a roofline object per kernel and the CPU oracle timed on the
 host cores; beside the timed steps, the sparse call on uniform random index sets of the same
-sizes (cold) and warm-cache timings of the main calls.
+sizes (cold) and warm-cache timings of the main calls.  `per_config` then repeats the indexer, the
+sparse attention, the one-call step and the dense baseline (fewer steps, same flush discipline) on
+the other decode settings: the tiny case, the Llama-3-8B- and Qwen2.5-72B-shaped batches at 50x,
+and the 16-request sweep at 10x/50x/100x/1000x sparsity (oracle top-k lists, plus uniform random
+sets of the same sizes for the sparse call).
 Call durations come from HIP events created with hipEventDisableSystemFence; an event pair
 around one call still counts about 4 µs of dispatch latency on top of the kernels' run time.
 """
@@ -43,7 +55,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode µs/step + gathered-KV GB/s (% HBM peak), speedup vs dense at 50×"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "llama3_8b_n32k_k655"
+DEFAULT_WORKLOAD = "ragged_paged_b32_t4"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "sparse_decode_attn": ["long_context_sparse_oracle_amd/csrc/attention.hip",
@@ -95,6 +107,9 @@ def parse():
                    help="skip the random-set and warm-cache timings after the steps (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle leg (0 disables it)")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip the other decode settings after the main workload (profiling runs)")
+    p.add_argument("--per-config-steps", type=int, default=10)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration runs)")
     return p.parse_args()
@@ -257,6 +272,128 @@ def cpu_baseline(wl, gathered_bytes, seconds):
             f"all {rows} rows: float64 NumPy oracle top-k + sparse attention, {elapsed:.1f} s"
         ),
     }
+
+
+# The other decode settings, each timed with the same flush discipline after the main workload:
+# (label, named workload, sweep level or None).  The sweep's K and V do not depend on k, so its
+# four sparsity levels share one draw.
+PER_CONFIG = [
+    ("tiny_d64_n1024", "tiny_d64_n1024", None),
+    ("llama3_8b_n32k_k655", "llama3_8b_n32k_k655", None),
+    ("qwen25_72b_n128k_k2621", "qwen25_72b_n128k_k2621", None),
+    ("sweep_b16_n128k_s10", "sweep_b16_n128k", "s10"),
+    ("sweep_b16_n128k_s50", "sweep_b16_n128k", "s50"),
+    ("sweep_b16_n128k_s100", "sweep_b16_n128k", "s100"),
+    ("sweep_b16_n128k_s1000", "sweep_b16_n128k", "s1000"),
+]
+
+
+def time_calls(calls, steps, warmup, flush, hev, sh):
+    """Mean µs of every call over `steps` iterations (after `warmup` untimed ones), each call
+    after a flush and between fence-free events on stream handle `sh`."""
+    import torch
+
+    for _ in range(warmup):
+        for fn in calls.values():
+            flush()
+            fn()
+    torch.cuda.synchronize()
+    evs = []
+    gc.collect()
+    gc.disable()
+    for _ in range(steps):
+        for name, fn in calls.items():
+            e0, e1 = hev.create(), hev.create()
+            flush()
+            hev.record(e0, sh)
+            fn()
+            hev.record(e1, sh)
+            evs.append((name, e0, e1))
+    torch.cuda.synchronize()
+    gc.enable()
+    times = {k: [] for k in calls}
+    for name, e0, e1 in evs:
+        times[name].append(hev.elapsed_us(e0, e1))
+        hev.destroy(e0)
+        hev.destroy(e1)
+    return {k: statistics.fmean(v) for k, v in times.items()}
+
+
+def per_config_results(args, flush, hev, sh):
+    """Indexer, sparse attention (oracle lists, and uniform random sets of the same sizes), the
+    one-call step and the dense baseline on every other decode setting."""
+    import dataclasses
+
+    import torch
+
+    import long_context_sparse_oracle_amd as cs
+    from workloads import make_named, random_index_sets
+    from workloads.synth import SWEEP_K
+
+    dev = torch.device("cuda", 0)
+    out = {}
+    drawn = {}
+    for label, name, level in PER_CONFIG:
+        if label == args.workload or (level and f"{name}_{level}" == f"{args.workload}_{args.sweep_k}"):
+            continue
+        print(f"[bench] per-config {label}", file=sys.stderr, flush=True)
+        if name not in drawn:
+            drawn.clear()
+            torch.cuda.empty_cache()
+            drawn[name] = make_named(name, device=dev)
+        wl = drawn[name]
+        if level:
+            k = SWEEP_K[level]
+            wl = dataclasses.replace(wl, k_per_req=torch.full_like(wl.k_per_req, k), k_max=k)
+        cache = cs.KVCache(wl.k_cache, wl.v_cache, wl.seq_lens, page_table=wl.page_table, max_len=wl.max_len)
+        B, T, Hq, d, k_max, kptr = wl.batch, wl.q_len, wl.num_q_heads, wl.head_dim, wl.k_max, wl.k_per_req
+        indices = torch.empty((B, T, Hq, k_max), dtype=torch.int32, device=dev)
+        o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+        ws_t = torch.empty(max(1, cs.topk_index_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(max(1, cs.sparse_decode_attn_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8,
+                           device=dev)
+        ws_d = torch.empty(max(1, cs.dense_decode_attn_workspace_size(wl.q, cache)), dtype=torch.uint8, device=dev)
+        ws_st = torch.empty(max(1, cs.sparse_decode_step_workspace_size(wl.q, cache, k_max)), dtype=torch.uint8,
+                            device=dev)
+        idx_rand = random_index_sets(wl)
+        calls = {
+            "topk_index": lambda: cs.topk_index(wl.q, cache, kptr, k_max=k_max, indices=indices, workspace=ws_t),
+            "sparse_decode_attn": lambda: cs.sparse_decode_attn(wl.q, cache, indices, out=o, lse=lse,
+                                                                workspace=ws_s),
+            "sparse_random_sets": lambda: cs.sparse_decode_attn(wl.q, cache, idx_rand, out=o, lse=lse,
+                                                                workspace=ws_s),
+            "sparse_decode_step": lambda: cs.sparse_decode_step(wl.q, cache, kptr, k_max=k_max, out=o, lse=lse,
+                                                                workspace=ws_st),
+            "dense_decode_attn": lambda: cs.dense_decode_attn(wl.q, cache, out=o, lse=lse, workspace=ws_d),
+        }
+        mean = time_calls(calls, args.per_config_steps, 3, flush, hev, sh)
+        ab = algorithmic_bytes(wl, indices, args.cand_mult)
+        ab_r = algorithmic_bytes(wl, idx_rand, args.cand_mult)
+        frac = lambda nbytes, us: round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)  # noqa: E731
+        dense = mean["dense_decode_attn"]
+        out[label] = {
+            "k": k_max,
+            "sparsity": round(wl.max_len / k_max, 1),
+            "sparse_us": round(mean["sparse_decode_attn"], 2),
+            "sparse_frac": frac(ab["sparse"], mean["sparse_decode_attn"]),
+            "sparse_random_sets_us": round(mean["sparse_random_sets"], 2),
+            "sparse_random_sets_frac": frac(ab_r["sparse"], mean["sparse_random_sets"]),
+            "topk_us": round(mean["topk_index"], 2),
+            "topk_frac": frac(ab["topk"], mean["topk_index"]),
+            "step_us": round(mean["sparse_decode_step"], 2),
+            "dense_us": round(dense, 2),
+            "dense_frac": frac(ab["dense"], dense),
+            "speedup_vs_dense": round(dense / mean["sparse_decode_attn"], 3),
+            "random_sets_speedup_vs_dense": round(dense / mean["sparse_random_sets"], 3),
+            "topk_plus_sparse_vs_dense": round(dense / (mean["topk_index"] + mean["sparse_decode_attn"]), 3),
+            "step_vs_dense": round(dense / mean["sparse_decode_step"], 3),
+            "gathered_bytes": ab["sparse"],
+        }
+        del calls, indices, o, lse, ws_t, ws_s, ws_d, ws_st, idx_rand, cache, wl
+    drawn.clear()
+    torch.cuda.empty_cache()
+    return out
 
 
 class HipEvents:
@@ -525,7 +662,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round((mean["topk_index"] + mean["sparse_decode_attn"] + mean["dense_decode_attn"]) / 1e3,
+                             4),
+        "wall_ms_per_iteration": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -584,6 +723,14 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(wl, ab["sparse"], args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
+    if not args.no_per_config:
+        # free the main workload before drawing the others
+        del calls, wl, cache, sketch, indices, out_s, lse_s, out_d, lse_d, ws_t, ws_s, ws_d, out_st, lse_st
+        del ws_st, idx_sk, ws_tk, out_sk, lse_sk, ws_sk
+        if random_sets is not None:
+            del idx_rand
+        torch.cuda.empty_cache()
+        rec["per_config"] = per_config_results(args, flush, hev2, sh)
     print(json.dumps(rec), flush=True)
 
 

@@ -106,15 +106,25 @@ def _generator(seed: int, tag: str, device) -> torch.Generator:
     return g
 
 
+# values per generator call when drawing N(0, 1) tensors (256 MB of float32 staging)
+_SLAB_VALUES = 1 << 26
+
+
 def _normal_bf16(shape: Sequence[int], gen: torch.Generator, device) -> torch.Tensor:
-    """i.i.d. N(0, 1) drawn in fp32 and rounded to bf16 (round to nearest even), one leading
-    slice at a time so the fp32 staging buffer stays small."""
+    """i.i.d. N(0, 1) drawn in fp32 and rounded to bf16 (round to nearest even).
+
+    The draw goes in slabs of whole leading slices, up to 2^26 values (256 MB of fp32 staging)
+    per call, so a paged pool of ~10^5 small pages costs a few dozen generator calls, not one per
+    page.  A tensor of at most 2^26 values is drawn in a single call."""
     out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=device)
     flat = out.view(shape[0], -1)
-    for i in range(shape[0]):
-        flat[i] = torch.randn(flat.shape[1], generator=gen, device=device, dtype=torch.float32).to(
-            torch.bfloat16
-        )
+    per_row = max(1, flat.shape[1])
+    rows_per_slab = max(1, _SLAB_VALUES // per_row)
+    for i in range(0, shape[0], rows_per_slab):
+        j = min(shape[0], i + rows_per_slab)
+        slab = torch.randn((j - i) * flat.shape[1], generator=gen, device=device, dtype=torch.float32)
+        flat[i:j] = slab.view(j - i, flat.shape[1]).to(torch.bfloat16)
+        del slab
     return out
 
 
