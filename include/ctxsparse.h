@@ -41,7 +41,9 @@ typedef enum {
   CS_ERR_INVALID_ARG = 1,         /* null pointer, non-positive or inconsistent size */
   CS_ERR_UNSUPPORTED = 2,         /* valid but not implemented: head_dim other than 64/128, ... */
   CS_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_workspace_size() figure */
-  CS_ERR_HIP = 4                  /* hipGetLastError() reported a launch failure */
+  CS_ERR_HIP = 4,                 /* hipGetLastError() reported a launch failure */
+  CS_ERR_SCRATCH_LIMIT = 5        /* sparse_decode_attn_noalloc: the call needs more scratch than
+                                     CS_NOALLOC_SCRATCH_BYTES */
 } cs_status;
 
 /* Problem shape of one decode step (host memory). */
@@ -125,6 +127,26 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
                              const int32_t* indices, int32_t k_max, float sm_scale,
                              int32_t num_splits, float* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_decode_attn_noalloc — sparse_decode_attn for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as sparse_decode_attn, without the
+ * workspace: the split partials live in a fixed static device buffer of the library,
+ * CS_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  A call whose split plan needs
+ * more (rows * splits * (d + 2) * 4 bytes, rounded up; only plans with splits > 1 use any) returns
+ * CS_ERR_SCRATCH_LIMIT with nothing queued; the automatic plan (num_splits = 0) needs at most
+ * about 270 KB.  Nothing is allocated or freed.  The first call on a device resolves the
+ * buffer's device address (hipGetSymbolAddress), so make that first call outside graph capture.
+ * Every call on one GPU shares that GPU's buffer: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and give wrong results.  Each call writes
+ * the partials it reads, so the contents left by an earlier call never matter.
+ * ------------------------------------------------------------------------------------------ */
+#define CS_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+cs_status sparse_decode_attn_noalloc(const cs_decode_shape* shape, const void* q,
+                                     const cs_kv_desc* kv, const int32_t* indices, int32_t k_max,
+                                     float sm_scale, int32_t num_splits, float* out, float* lse,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * sparse_decode_step — the oracle-indexed decode step in one call: topk_index followed by

@@ -26,6 +26,7 @@ _BINDING_NAMES = (
     "topk_index_workspace_size",
     "sparse_decode_attn",
     "sparse_decode_attn_workspace_size",
+    "sparse_decode_attn_noalloc",
     "dense_decode_attn",
     "dense_decode_attn_workspace_size",
     "sparse_decode_step",

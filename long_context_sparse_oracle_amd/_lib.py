@@ -26,6 +26,7 @@ STATUS_NAMES = {
     2: "CS_ERR_UNSUPPORTED",
     3: "CS_ERR_WORKSPACE_TOO_SMALL",
     4: "CS_ERR_HIP",
+    5: "CS_ERR_SCRATCH_LIMIT",
 }
 EXPORTS = (
     "cs_status_str",
@@ -34,6 +35,7 @@ EXPORTS = (
     "topk_index",
     "sparse_decode_attn_workspace_size",
     "sparse_decode_attn",
+    "sparse_decode_attn_noalloc",
     "dense_decode_attn_workspace_size",
     "dense_decode_attn",
     "sparse_decode_step_workspace_size",
@@ -98,6 +100,8 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_workspace_size.restype = sz
     lib.sparse_decode_attn.argtypes = [shp, P, kvp, P, i32, f32, i32, P, P, P, sz, P]
     lib.sparse_decode_attn.restype = ctypes.c_int
+    lib.sparse_decode_attn_noalloc.argtypes = [shp, P, kvp, P, i32, f32, i32, P, P, P]
+    lib.sparse_decode_attn_noalloc.restype = ctypes.c_int
     lib.dense_decode_attn_workspace_size.argtypes = [shp, kvp, i32]
     lib.dense_decode_attn_workspace_size.restype = sz
     lib.dense_decode_attn.argtypes = [shp, P, kvp, f32, i32, P, P, P, sz, P]
@@ -310,6 +314,31 @@ def sparse_decode_attn(
                                 int(num_splits), out.data_ptr(), lse.data_ptr(), wptr, wbytes,
                                 _stream(q))
     _check("sparse_decode_attn", st)
+    return out, lse
+
+
+def sparse_decode_attn_noalloc(
+    q: torch.Tensor,
+    cache: KVCache,
+    indices: torch.Tensor,
+    *,
+    sm_scale: Optional[float] = None,
+    num_splits: int = 0,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """sparse_decode_attn without a workspace: the split partials go to the library's fixed
+    per-GPU scratch buffer.  Pass `out` and `lse` to allocate nothing at all."""
+    shp = _shape(q, cache)
+    if indices.dtype != torch.int32 or indices.dim() != 4 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous int32 tensor [B, T, Hq, k_max]")
+    k_max = int(indices.shape[3])
+    out, lse = _outputs(shp, q.device, out, lse)
+    desc = cache.desc()
+    st = LIB.sparse_decode_attn_noalloc(ctypes.byref(shp), q.data_ptr(), ctypes.byref(desc),
+                                        indices.data_ptr(), k_max, _scale(shp.head_dim, sm_scale),
+                                        int(num_splits), out.data_ptr(), lse.data_ptr(), _stream(q))
+    _check("sparse_decode_attn_noalloc", st)
     return out, lse
 
 

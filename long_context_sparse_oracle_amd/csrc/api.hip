@@ -9,6 +9,11 @@
 #include "../../include/ctxsparse.h"
 #include "launch.h"
 
+// Fixed device scratch of sparse_decode_attn_noalloc (split partials), one copy per GPU, held
+// until the process ends.  Host code never uses this name as an address: the device address is
+// resolved per device with hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[CS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxGT = 64;             // query rows per KV head (G * T): four 16-row MFMA tiles
@@ -297,6 +302,26 @@ size_t attn_ws(const cs_decode_shape* s, int S) {
   return align_up(rows * S * (size_t)s->head_dim * sizeof(float)) + align_up(rows * S * 2 * sizeof(float));
 }
 
+// Device address of `scratch` on the current device, resolved on the first call on that device
+// and kept per device (each GPU holds its own copy at its own address).
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 cs_status check_ws(void* ws, size_t bytes, size_t need) {
   if (need == 0) return CS_OK;
   if (!ws || !aligned(ws, 16)) return CS_ERR_INVALID_ARG;
@@ -452,6 +477,7 @@ const char* cs_status_str(cs_status s) {
     case CS_ERR_UNSUPPORTED: return "CS_ERR_UNSUPPORTED";
     case CS_ERR_WORKSPACE_TOO_SMALL: return "CS_ERR_WORKSPACE_TOO_SMALL";
     case CS_ERR_HIP: return "CS_ERR_HIP";
+    case CS_ERR_SCRATCH_LIMIT: return "CS_ERR_SCRATCH_LIMIT";
   }
   return "CS_ERR_UNKNOWN";
 }
@@ -506,6 +532,26 @@ cs_status sparse_decode_attn(const cs_decode_shape* shape, const void* q, const 
   if ((st = check_ws(workspace, workspace_bytes, need)) != CS_OK) return st;
 
   cs::AttnLaunch a = sparse_launch(shape, q, kv, indices, k_max, sm_scale, plan, out, lse, workspace);
+  hipError_t e = cs::launch_sparse(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CS_OK : CS_ERR_HIP;
+}
+
+cs_status sparse_decode_attn_noalloc(const cs_decode_shape* shape, const void* q, const cs_kv_desc* kv,
+                                     const int32_t* indices, int32_t k_max, float sm_scale,
+                                     int32_t num_splits, float* out, float* lse, void* stream) {
+  cs_status st = check_shape(shape);
+  if (st != CS_OK) return st;
+  if ((st = check_kv(shape, kv)) != CS_OK) return st;
+  if (!q || !indices || !out || !lse) return CS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return CS_ERR_INVALID_ARG;
+  if (k_max < 1 || num_splits < 0 || !std::isfinite(sm_scale)) return CS_ERR_INVALID_ARG;
+  const SparsePlan plan = sparse_plan(shape, k_max, num_splits);
+  if (attn_ws(shape, plan.S) > CS_NOALLOC_SCRATCH_BYTES) return CS_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (plan.S > 1 && noalloc_scratch(&ws) != hipSuccess) return CS_ERR_HIP;
+  // the partials of every split are written before the combine reads them: nothing to clear
+  cs::AttnLaunch a = sparse_launch(shape, q, kv, indices, k_max, sm_scale, plan, out, lse, ws);
   hipError_t e = cs::launch_sparse(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CS_OK : CS_ERR_HIP;
 }

@@ -33,7 +33,8 @@ def test_header_declares_entry_points():
               "sparse_decode_attn_workspace_size", "dense_decode_attn_workspace_size",
               "sparse_decode_step", "sparse_decode_step_workspace_size", "key_sketch_build",
               "topk_index_sketch", "topk_index_sketch_workspace_size", "sparse_decode_step_sketch",
-              "sparse_decode_step_sketch_workspace_size", "cs_status_str", "cs_version"):
+              "sparse_decode_step_sketch_workspace_size", "cs_status_str", "cs_version",
+              "sparse_decode_attn_noalloc"):
         assert n in names
 
 
@@ -180,6 +181,34 @@ def test_attention_arguments(lib):
     need = L.dense_decode_attn_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 4)
     assert need > 0
     assert _dense(L, _shape(), _kv(), splits=4, ws_bytes=need - 1) == WS_SMALL
+
+
+SCRATCH_LIMIT = 5
+
+
+def _noalloc(L, shape, kv, k_max=10, splits=0, idx=FAKE, out=FAKE, lse=FAKE, q=FAKE, scale=0.088):
+    return L.sparse_decode_attn_noalloc(ctypes.byref(shape), q, ctypes.byref(kv), idx, k_max, scale, splits,
+                                        out, lse, None)
+
+
+def test_noalloc_arguments_and_scratch_limit(lib):
+    L = lib.LIB
+    assert _noalloc(L, _shape(d=96), _kv()) == UNSUPPORTED
+    assert _noalloc(L, _shape(), _kv(k=0)) == INVALID
+    assert _noalloc(L, _shape(), _kv(), k_max=0) == INVALID
+    assert _noalloc(L, _shape(), _kv(), splits=-1) == INVALID
+    assert _noalloc(L, _shape(), _kv(), idx=0) == INVALID
+    assert _noalloc(L, _shape(), _kv(), out=0) == INVALID
+    assert _noalloc(L, _shape(), _kv(), lse=FAKE + 2) == INVALID
+    assert _noalloc(L, _shape(), _kv(), q=FAKE + 4) == INVALID
+    assert _noalloc(L, _shape(), _kv(), scale=float("nan")) == INVALID
+    # a split plan whose partials exceed the fixed 4 MiB scratch is refused before any GPU work:
+    # 16 rows x 1000 splits x (128 + 2) floats = 8.3 MB
+    limit = 4 << 20
+    need = L.sparse_decode_attn_workspace_size(ctypes.byref(_shape()), 1000, 1000)
+    assert need > limit
+    assert _noalloc(L, _shape(), _kv(), k_max=1000, splits=1000) == SCRATCH_LIMIT
+    assert L.cs_status_str(SCRATCH_LIMIT).decode() == "CS_ERR_SCRATCH_LIMIT"
 
 
 def _step(L, shape, kv, k_max=10, scale=0.088, ws=FAKE, ws_bytes=1 << 40, q=FAKE, idx=None, out=FAKE,
