@@ -86,3 +86,38 @@ def test_profile_harness_groups_and_names_calls():
     assert segs[1][1] == {"cs::sample_tau_kernel<128, false, false>": 1.0,
                           "cs::score_cand_kernel<128, false, 1, false>": 1.0,
                           "cs::cand_select_kernel<128, false, false, 3>": 1.0}
+
+
+def test_profile_counter_parsing_groups_calls_and_counters(tmp_path):
+    """bench_profile's counter parser: one row per (dispatch, counter), calls separated by the
+    flush kernels, the calibration copy picked out, every counter kept apart."""
+    import csv
+
+    import bench_profile as bp
+
+    rows = []
+    disp = [
+        (1, "void at::native::reduce_kernel<512, 1>(...)", 10),
+        (2, "void cs::sparse_partial_kernel<128, true, 16, 8>(...)", 20),
+        (3, "void at::native::reduce_kernel<512, 1>(...)", 30),
+        (4, "void cs::score_cand_kernel<128, true, 4, false, false>(...)", 40),
+        (5, "void cs::cand_select_kernel<128, true, false, 3>(...)", 50),
+        (6, "void at::native::reduce_kernel<512, 1>(...)", 60),
+        (7, "__amd_rocclr_copyBuffer", 70),
+    ]
+    vals = {"TCC_HIT_sum": {2: 30.0, 4: 5.0, 5: 7.0, 7: 2e6}, "TCC_MISS_sum": {2: 70.0, 4: 95.0, 5: 3.0, 7: 1e6}}
+    for did, name, ts in disp:
+        for cname, per in vals.items():
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": cname,
+                         "Counter_Value": per.get(did, 1.0), "Start_Timestamp": ts, "End_Timestamp": ts + 1})
+    d = tmp_path / "l2"
+    d.mkdir()
+    with open(d / "l2_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        w.writerows(rows)
+    per_call, per_kernel, calib = bp.counters(str(d), ["TCC_HIT_sum", "TCC_MISS_sum"])
+    assert per_call["TCC_HIT_sum"]["sparse_decode_attn"] == 30.0
+    assert per_call["TCC_MISS_sum"]["topk_index"] == 98.0
+    assert per_kernel["TCC_HIT_sum"]["topk_index"]["cs::cand_select_kernel<128, true, false, 3>"] == 7.0
+    assert calib == {"TCC_HIT_sum": 2e6, "TCC_MISS_sum": 1e6}
