@@ -279,6 +279,11 @@ int dense_splits(const cs_decode_shape* s, const cs_kv_desc* kv, int requested, 
   } else {
     const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
     S = ceil_div(4LL * cu_count(), groups);
+    // chunks of at most 16384 positions: in a ragged batch a workgroup's chunk may be the last
+    // one still streaming, and longer chunks leave a long tail (32 requests of 8192-131072
+    // positions: 1837 us with 32768-position chunks, 1673 us with 16384)
+    const int64_t min_S = ceil_div(kv->max_len, 16384);
+    if (S < min_S) S = min_S;
     const int64_t by_len = ceil_div(kv->max_len, 256);
     if (S > by_len) S = by_len;
   }

@@ -309,8 +309,8 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_kernel(
   __shared__ float red_l[kAttnWaves][16];
   __shared__ float red_o[kAttnWaves][MR][D];
 
-  const int s = blockIdx.x;
   const int bh = blockIdx.y;
+  const int s = rotated_chunk(blockIdx.x, bh, gridDim.x);
   const int mt = blockIdx.z;
   const int Hkv = kv.num_kv_heads;
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
@@ -517,8 +517,8 @@ __global__ __launch_bounds__(kAttnThreads) void dense_partial_mfma_kernel(
   __shared__ float red_m[kAttnWaves][16];
   __shared__ float red_l[kAttnWaves][16];
 
-  const int s = blockIdx.x;
   const int bh = blockIdx.y;
+  const int s = rotated_chunk(blockIdx.x, bh, gridDim.x);
   const int mt = blockIdx.z;
   const int Hkv = kv.num_kv_heads;
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;

@@ -218,6 +218,19 @@ __device__ __forceinline__ int64_t kv_tile_staged(const KVArgs& kv, const int* l
   }
 }
 
+// Chunk of a (request, KV head) group that the workgroup in chunk slot `slot` (blockIdx.x of a
+// (chunks, groups, tiles) grid) streams: the slots of a group are rotated by the group index.
+// Workgroups go to the 8 XCDs round-robin by linear id, so with the plain order chunk c of every
+// group ran on XCD c mod 8 (chunk counts are mostly multiples of 8); in a ragged batch, whose
+// late chunks are mostly empty, the XCDs holding late chunks idled (32 requests of 8192-131072
+// positions: the indexer's K stream at 3.4 TB/s).  Rotated, XCD x gets chunk x - g (mod 8) of
+// group g, the same mix of early and late chunks on every XCD, while a group's chunks are still
+// dispatched together (concurrent workgroups sweep neighbouring addresses: the same chunks
+// ordered group-major over the whole grid streamed 4-6% slower on full-length caches).
+__device__ __forceinline__ int rotated_chunk(int slot, int group, int chunks) {
+  return (int)(((unsigned)slot + (unsigned)group) % (unsigned)chunks);
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

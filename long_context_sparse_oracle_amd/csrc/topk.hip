@@ -83,8 +83,8 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
   extern __shared__ uint32_t lds_hist[];  // [hist_rows][kHistBins / 2], then the chunk's page ids
   int* lds_pages = reinterpret_cast<int*>(lds_hist + hist_rows * (kHistBins / 2));
   constexpr int KS = SK ? D / 64 : D / 32;  // MFMA k-steps per tile
-  const int c = blockIdx.x;
   const int bh = blockIdx.y;
+  const int c = rotated_chunk(blockIdx.x, bh, gridDim.x);
   const int mt = blockIdx.z;
   const int Hkv = kv.num_kv_heads;
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
@@ -936,8 +936,8 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
   __shared__ float tau_sh[16];                                 // PREFIX: the tile's thresholds
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int UNR = kScoreUnroll;  // tiles per step (twice as many for the sketch measured no faster)
-  const int c = blockIdx.x;
   const int bh = blockIdx.y;
+  const int c = rotated_chunk(blockIdx.x, bh, gridDim.x);
   const int mt = blockIdx.z;
   const int Hkv = kv.num_kv_heads;
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
