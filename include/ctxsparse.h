@@ -42,8 +42,12 @@ typedef enum {
   CS_ERR_UNSUPPORTED = 2,         /* valid but not implemented: head_dim other than 64/128, ... */
   CS_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_workspace_size() figure */
   CS_ERR_HIP = 4,                 /* hipGetLastError() reported a launch failure */
-  CS_ERR_SCRATCH_LIMIT = 5        /* sparse_decode_attn_noalloc: the call needs more scratch than
+  CS_ERR_SCRATCH_LIMIT = 5,       /* sparse_decode_attn_noalloc: the call needs more scratch than
                                      CS_NOALLOC_SCRATCH_BYTES */
+  /* not statuses: they give the type the range of a 32-bit int, so any int a caller passes to
+     cs_status_str is a valid value of the type */
+  CS_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  CS_STATUS_RANGE_MAX_ = 2147483647
 } cs_status;
 
 /* Problem shape of one decode step (host memory). */
