@@ -33,7 +33,8 @@ sizes (cold) and warm-cache timings of the main calls.  `per_config` then repeat
 sparse attention, the one-call step and the dense baseline (fewer steps, same flush discipline) on
 the other decode settings: the tiny case, the Llama-3-8B- and Qwen2.5-72B-shaped batches at 50x,
 and the 16-request sweep at 10x/50x/100x/1000x sparsity (oracle top-k lists, plus uniform random
-sets of the same sizes for the sparse call).
+sets of the same sizes for the sparse call), with the reduced-byte indexer's one-call step at
+cand_mult 1 and 2 (each with the per-step sketch update) and the recall of its cand_mult-1 lists.
 Call durations come from HIP events created with hipEventDisableSystemFence; an event pair
 around one call still counts about 4 µs of dispatch latency on top of the kernels' run time.
 """
@@ -333,12 +334,14 @@ def per_config_results(args, flush, hev, sh):
     dev = torch.device("cuda", 0)
     out = {}
     drawn = {}
+    sketches = {}
     for label, name, level in PER_CONFIG:
         if label == args.workload or (level and f"{name}_{level}" == f"{args.workload}_{args.sweep_k}"):
             continue
         print(f"[bench] per-config {label}", file=sys.stderr, flush=True)
         if name not in drawn:
             drawn.clear()
+            sketches.clear()
             torch.cuda.empty_cache()
             drawn[name] = make_named(name, device=dev)
         wl = drawn[name]
@@ -368,6 +371,30 @@ def per_config_results(args, flush, hev, sh):
             "dense_decode_attn": lambda: cs.dense_decode_attn(wl.q, cache, out=o, lse=lse, workspace=ws_d),
         }
         mean = time_calls(calls, args.per_config_steps, 3, flush, hev, sh)
+        # the reduced-byte indexer's step at cand_mult 1 and 2, with the per-step sketch update
+        if name not in sketches:
+            sketches.clear()
+            sketches[name] = cs.key_sketch_build(cache)
+        sk = sketches[name]
+        idx_m1 = torch.empty_like(indices)
+        ws_k1 = torch.empty(max(1, cs.topk_index_sketch_workspace_size(wl.q, cache, k_max, 1)), dtype=torch.uint8,
+                            device=dev)
+        ws_s1 = torch.empty(max(1, cs.sparse_decode_step_sketch_workspace_size(wl.q, cache, k_max, 1)),
+                            dtype=torch.uint8, device=dev)
+        ws_s2 = torch.empty(max(1, cs.sparse_decode_step_sketch_workspace_size(wl.q, cache, k_max, 2)),
+                            dtype=torch.uint8, device=dev)
+        sk_calls = {
+            "update": lambda: cs.key_sketch_build(cache, sk, last_n=wl.q_len),
+            "step_m1": lambda: cs.sparse_decode_step_sketch(wl.q, cache, sk, kptr, k_max=k_max, cand_mult=1, out=o,
+                                                            lse=lse, workspace=ws_s1),
+            "step_m2": lambda: cs.sparse_decode_step_sketch(wl.q, cache, sk, kptr, k_max=k_max, cand_mult=2, out=o,
+                                                            lse=lse, workspace=ws_s2),
+        }
+        skm = time_calls(sk_calls, args.per_config_steps, 2, flush, hev, sh)
+        cs.topk_index_sketch(wl.q, cache, sk, kptr, k_max=k_max, cand_mult=1, indices=idx_m1, workspace=ws_k1)
+        torch.cuda.synchronize()
+        rec_m1 = recall(idx_m1, indices, wl.max_len)
+        del idx_m1, ws_k1, ws_s1, ws_s2, sk_calls
         ab = algorithmic_bytes(wl, indices, args.cand_mult)
         ab_r = algorithmic_bytes(wl, idx_rand, args.cand_mult)
         frac = lambda nbytes, us: round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)  # noqa: E731
@@ -388,10 +415,17 @@ def per_config_results(args, flush, hev, sh):
             "random_sets_speedup_vs_dense": round(dense / mean["sparse_random_sets"], 3),
             "topk_plus_sparse_vs_dense": round(dense / (mean["topk_index"] + mean["sparse_decode_attn"]), 3),
             "step_vs_dense": round(dense / mean["sparse_decode_step"], 3),
+            "sketch_update_us": round(skm["update"], 2),
+            "sketch_m1_step_us": round(skm["step_m1"], 2),
+            "sketch_m1_step_vs_dense": round(dense / (skm["step_m1"] + skm["update"]), 3),
+            "sketch_m1_recall": round(rec_m1, 5),
+            "sketch_m2_step_us": round(skm["step_m2"], 2),
+            "sketch_m2_step_vs_dense": round(dense / (skm["step_m2"] + skm["update"]), 3),
             "gathered_bytes": ab["sparse"],
         }
         del calls, indices, o, lse, ws_t, ws_s, ws_d, ws_st, idx_rand, cache, wl
     drawn.clear()
+    sketches.clear()
     torch.cuda.empty_cache()
     return out
 
@@ -604,6 +638,10 @@ def main():
             hev2.destroy(e1)
         return statistics.fmean(ts)
 
+    # the reduced-byte indexer's lists and outputs against the exact ones, before the extras below
+    # reuse its buffers
+    sk_recall = recall(idx_sk, indices, wl.max_len)
+    sk_out_diff = float((out_sk - out_st).abs().max())
     # Beside the timed steps (not part of `value`): the sparse call on uniform random index sets of
     # the same sizes (drawn without replacement), cold; and warm-cache timings of the main calls.
     from workloads import random_index_sets
@@ -622,6 +660,23 @@ def main():
             "pct_hbm_peak": round(100.0 * rand_gbs / HBM_PEAK_GBS, 2),
             "speedup_vs_dense": round(mean_of(times["dense_decode_attn"]) / rand_us, 3),
         }
+    # the reduced-byte indexer without re-rank (cand_mult = 1: the sketch's own top-k), cold
+    sketch_m1 = None
+    if not args.no_extras:
+        idx_m1 = torch.empty_like(indices)
+        ws_m1 = torch.empty(max(1, cs.topk_index_sketch_workspace_size(wl.q, cache, k_max, 1)), dtype=torch.uint8,
+                            device=dev)
+        ws_m1s = torch.empty(max(1, cs.sparse_decode_step_sketch_workspace_size(wl.q, cache, k_max, 1)),
+                             dtype=torch.uint8, device=dev)
+        n_ex = max(args.steps // 2, 5)
+        m1_topk = timed(lambda: cs.topk_index_sketch(wl.q, cache, sketch, kptr, k_max=k_max, cand_mult=1,
+                                                     indices=idx_m1, workspace=ws_m1), n_ex, True)
+        m1_step = timed(lambda: cs.sparse_decode_step_sketch(wl.q, cache, sketch, kptr, k_max=k_max, cand_mult=1,
+                                                             out=out_sk, lse=lse_sk, workspace=ws_m1s), n_ex, True)
+        torch.cuda.synchronize()
+        sketch_m1 = {"topk_us": round(m1_topk, 2), "step_us": round(m1_step, 2),
+                     "recall_vs_exact_topk": round(recall(idx_m1, indices, wl.max_len), 5)}
+        del ws_m1, ws_m1s
     warm = None
     if flush_buf is not None and not args.no_extras:
         warm = {}
@@ -638,8 +693,6 @@ def main():
     build_us = hev2.elapsed_us(eb0, eb1)
     hev2.destroy(eb0)
     hev2.destroy(eb1)
-    sk_recall = recall(idx_sk, indices, wl.max_len)
-    sk_out_diff = float((out_sk - out_st).abs().max())
     mean = {k: statistics.fmean(v) for k, v in times.items()}
     med = {k: statistics.median(v) for k, v in times.items()}
     traffic = load_traffic()
@@ -696,6 +749,9 @@ def main():
             "recall_vs_exact_topk": round(sk_recall, 5),
             "max_abs_out_diff_vs_exact_step": sk_out_diff,
             "rerank_rows": ab["rerank_rows"],
+            "m1": None if sketch_m1 is None else dict(
+                sketch_m1, step_speedup_vs_dense=round(mean["dense_decode_attn"] /
+                                                       (sketch_m1["step_us"] + mean["key_sketch_update"]), 3)),
         },
         "pct_hbm_peak": round(100.0 * sparse_gbs / HBM_PEAK_GBS, 2),
         "percentiles_us": {name: percentiles(v) for name, v in times.items()},
@@ -729,6 +785,8 @@ def main():
         del ws_st, idx_sk, ws_tk, out_sk, lse_sk, ws_sk
         if random_sets is not None:
             del idx_rand
+        if sketch_m1 is not None:
+            del idx_m1
         torch.cuda.empty_cache()
         rec["per_config"] = per_config_results(args, flush, hev2, sh)
     print(json.dumps(rec), flush=True)
