@@ -218,6 +218,25 @@ __device__ __forceinline__ int64_t kv_tile_staged(const KVArgs& kv, const int* l
   }
 }
 
+// Row (b * T + t) * Hq + hq handled by workgroup `wid` of a per-row grid of
+// grouped_row_blocks() workgroups: the G * T rows of one (request, KV head) group run on one XCD
+// (workgroups go to the 8 XCDs round-robin by linear id; group g takes the ids congruent to
+// g mod 8), so rows of a GQA group that read the same token find its lines in that XCD's L2.
+// -1 for the padding workgroups of the last groups.
+__device__ __forceinline__ int grouped_row(int wid, int B, int T, int Hq, int G, int Hkv) {
+  const int GT = G * T;
+  const int xcd = wid & 7, j = wid >> 3;
+  const int lg = j / GT, r = j - (j / GT) * GT;
+  const int g = lg * 8 + xcd;
+  if (g >= B * Hkv) return -1;
+  const int b = g / Hkv, h = g - (g / Hkv) * Hkv;
+  const int t = r / G, gi = r - (r / G) * G;
+  return (b * T + t) * Hq + h * G + gi;
+}
+__host__ __device__ inline unsigned grouped_row_blocks(int B, int Hkv, int GT) {
+  return 8u * (unsigned)((B * Hkv + 7) / 8) * (unsigned)GT;
+}
+
 // Chunk of a (request, KV head) group that the workgroup in chunk slot `slot` (blockIdx.x of a
 // (chunks, groups, tiles) grid) streams: the slots of a group are rotated by the group index.
 // Workgroups go to the 8 XCDs round-robin by linear id, so with the plain order chunk c of every

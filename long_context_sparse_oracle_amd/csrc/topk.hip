@@ -1544,13 +1544,14 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     const int32_t* __restrict__ k_per_req, float* __restrict__ region, int64_t score_stride,
     const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int lds_cap,
     int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int B) {
   extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
   __shared__ SelShared sh;
   __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
   uint32_t* lds_key = smem;
   uint32_t* hist = smem + lds_cap;
-  const int row = blockIdx.x;
+  const int row = grouped_row(blockIdx.x, B, T, Hq, G, kv.num_kv_heads);
+  if (row < 0) return;
   const int b = row / (T * Hq);
   const int t = (row / Hq) - (row / (T * Hq)) * T;
   const int hq = row - (row / Hq) * Hq;
@@ -1623,9 +1624,10 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(kCsThreads) void attend_scores_kernel(
     KVArgs kv, int T, int Hq, int G, const int32_t* __restrict__ k_per_req, int k_max,
     const int32_t* __restrict__ indices, const float* __restrict__ scores, int64_t score_stride,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int B) {
   __shared__ float red[kCsWaves * (D + 2)];
-  const int row = blockIdx.x;
+  const int row = grouped_row(blockIdx.x, B, T, Hq, G, kv.num_kv_heads);
+  if (row < 0) return;
   const int b = row / (T * Hq);
   const int t = (row / Hq) - (row / (T * Hq)) * T;
   const int hq = row - (row / Hq) * Hq;
@@ -1742,13 +1744,14 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
     const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int cand_mult, int lds_cap,
     int32_t* __restrict__ list_pos, float* __restrict__ list_score, int list_stride, bool listed,
     int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int B) {
   extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
   __shared__ SelShared sh;
   __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
   uint32_t* lds_key = smem;
   uint32_t* hist = smem + lds_cap;
-  const int row = blockIdx.x;
+  const int row = grouped_row(blockIdx.x, B, T, Hq, G, kv.num_kv_heads);
+  if (row < 0) return;
   const int b = row / (T * Hq);
   const int t = (row / Hq) - (row / (T * Hq)) * T;
   const int hq = row - (row / Hq) * Hq;
@@ -1943,10 +1946,10 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
       e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.sk, a.T, a.Hq, a.G,
-                       a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                       a.cand_chunks, a.k_max, a.cand_mult, lds_cap, a.list_pos, a.list_score,
-                       a.list_stride, listed, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
+    hipLaunchKernelGGL(sel, dim3(grouped_row_blocks(a.B, a.kv.num_kv_heads, a.GT)), dim3(kCsThreads), lds, stream,
+                       a.q, a.kv, a.sk, a.T, a.Hq, a.G, a.scale, a.k_per_req, a.scores, a.score_stride, a.counts,
+                       a.cand_chunk, a.cand_chunks, a.k_max, a.cand_mult, lds_cap, a.list_pos, a.list_score,
+                       a.list_stride, listed, a.indices, a.sel_pos, a.sel_score, a.out, a.lse, a.B);
   } else {
     auto sel = a.fused ? (big ? cand_select_kernel<D, PAGED, true, kCsBlocksBig> : cand_select_kernel<D, PAGED, true, kCsBlocks>)
                        : (big ? cand_select_kernel<D, PAGED, false, kCsBlocksBig> : cand_select_kernel<D, PAGED, false, kCsBlocks>);
@@ -1954,9 +1957,10 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
       e = hipFuncSetAttribute((const void*)sel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sel, dim3(a.rows), dim3(kCsThreads), lds, stream, a.q, a.kv, a.T, a.Hq, a.G,
-                       a.scale, a.k_per_req, a.scores, a.score_stride, a.counts, a.cand_chunk,
-                       a.cand_chunks, a.k_max, lds_cap, a.indices, a.sel_pos, a.sel_score, a.out, a.lse);
+    hipLaunchKernelGGL(sel, dim3(grouped_row_blocks(a.B, a.kv.num_kv_heads, a.GT)), dim3(kCsThreads), lds, stream,
+                       a.q, a.kv, a.T, a.Hq, a.G, a.scale, a.k_per_req, a.scores, a.score_stride, a.counts,
+                       a.cand_chunk, a.cand_chunks, a.k_max, lds_cap, a.indices, a.sel_pos, a.sel_score, a.out,
+                       a.lse, a.B);
   }
   return hipGetLastError();
 }
@@ -1970,8 +1974,9 @@ static hipError_t launch_filtered(const TopkLaunch& a, hipStream_t stream) {
 
 hipError_t launch_attend_scores(const TopkLaunch& a, hipStream_t stream) {
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(a.rows), dim3(kCsThreads), 0, stream, a.kv, a.T, a.Hq, a.G, a.k_per_req, a.k_max,
-                       a.indices, a.scores, a.score_stride, a.out, a.lse);
+    hipLaunchKernelGGL(kern, dim3(grouped_row_blocks(a.B, a.kv.num_kv_heads, a.GT)), dim3(kCsThreads), 0, stream,
+                       a.kv, a.T, a.Hq, a.G, a.k_per_req, a.k_max, a.indices, a.scores, a.score_stride, a.out,
+                       a.lse, a.B);
   };
   if (a.D == 128) {
     if (a.paged) go(attend_scores_kernel<128, true>); else go(attend_scores_kernel<128, false>);
