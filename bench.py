@@ -683,6 +683,14 @@ def main():
         for name in ("topk_index", "sparse_decode_attn", "dense_decode_attn", "sparse_decode_step"):
             calls[name]()
             warm[name] = round(timed(calls[name], 5, False), 2)
+    # the HBM read rate a plain streaming kernel reaches on this GPU: the flush itself (a sum over
+    # 2 GiB read from cold caches), timed after a flush
+    read_ceiling = None
+    if flush_buf is not None and not args.no_extras:
+        fl_us = timed(flush, 5, True)
+        gbs = flush_buf.numel() * 8 / (fl_us * 1e-6) / 1e9
+        read_ceiling = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "how": "torch.sum over a 2 GiB int64 buffer from cold caches, HIP events"}
     # one full build of the sketch (every cached key), timed on its own after the steps
     eb0, eb1 = hev2.create(), hev2.create()
     flush()
@@ -757,6 +765,7 @@ def main():
         "percentiles_us": {name: percentiles(v) for name, v in times.items()},
         "random_sets": random_sets,
         "warm_us": warm,
+        "hbm_read_ceiling": read_ceiling,
         "kernel_us_per_step": round(sum(mean.values()), 2),
         "gathered_bytes": ab["sparse"],
         "algorithmic_bytes": {"topk_index": ab["topk"], "sparse_decode_attn": ab["sparse"],
