@@ -1171,6 +1171,7 @@ constexpr int kCsThreads = 512;
 constexpr int kCsWaves = kCsThreads / kWave;
 constexpr int kMaxCandSlots = (262144 / 1024) * kCandWaves;  // chunks of >= 1024 positions
 constexpr int kCsPer = 8;  // consecutive items per thread in the ordered passes
+constexpr int kFallbackUnroll = 8;  // key rows per lane group in flight when a row is rescored whole
 
 // Candidates of a row in position order, from the slots: item f lives in the slot s with
 // prefix[s] <= f < prefix[s + 1].  Keys come from LDS when lds_key is set.
@@ -1590,17 +1591,27 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     const int p = lane / LPP, cdim = lane - (lane / LPP) * LPP;
     const int h = hq / G;
     const uint4 qv = ld16(q + (int64_t)row * D + cdim * 8);
-    for (int n0 = wave * PPW; n0 < vis; n0 += kCsWaves * PPW) {
-      const int n = n0 + p;
-      const bool ok = n < vis;
-      const uint4 kr = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, ok ? n : 0) + cdim * 8);
-      float dot = 0.f;
-      dot = dot2_bf16(qv.x, kr.x, dot);
-      dot = dot2_bf16(qv.y, kr.y, dot);
-      dot = dot2_bf16(qv.z, kr.z, dot);
-      dot = dot2_bf16(qv.w, kr.w, dot);
-      dot = group_sum<LPP>(dot);
-      if (ok && cdim == 0) srow[n] = dot * scale;
+    // kFallbackUnroll rows per lane group in flight (one at a time, a 10^5-position row took
+    // milliseconds on one workgroup)
+    constexpr int U = kFallbackUnroll, STRIDE = kCsWaves * PPW;
+    for (int n0 = wave * PPW; n0 < vis; n0 += STRIDE * U) {
+      uint4 kr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * STRIDE + p;
+        kr[u] = ld16(kv.k + kv_row<D, PAGED>(kv, b, h, n < vis ? n : 0) + cdim * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * STRIDE + p;
+        float dot = 0.f;
+        dot = dot2_bf16(qv.x, kr[u].x, dot);
+        dot = dot2_bf16(qv.y, kr[u].y, dot);
+        dot = dot2_bf16(qv.z, kr[u].z, dot);
+        dot = dot2_bf16(qv.w, kr[u].w, dot);
+        dot = group_sum<LPP>(dot);
+        if (n < vis && cdim == 0) srow[n] = dot * scale;
+      }
     }
     __syncthreads();
     select_ordered(DenseSource{srow}, vis, kk, k_max, so, hist, sh);
@@ -1673,18 +1684,28 @@ __device__ void sketch_row_scores(const KVArgs& kv, const SketchArgs& sk, int b,
   const int p = lane / LPP, c = lane - (lane / LPP) * LPP;
   const uint4 qc = ld16i8(sk.q_codes + qr * D + c * 16);
   const float qs = sk.q_scales[qr];
-  for (int n0 = wave * PPW; n0 < vis; n0 += kCsWaves * PPW) {
-    const int n = n0 + p;
-    const bool ok = n < vis;
-    const int64_t off = kv_row<D, PAGED>(kv, b, h, ok ? n : 0);
-    const uint4 kc = ld16i8(sk.codes + off + c * 16);
-    int d = 0;
-    d = __builtin_amdgcn_sdot4((int)qc.x, (int)kc.x, d, false);
-    d = __builtin_amdgcn_sdot4((int)qc.y, (int)kc.y, d, false);
-    d = __builtin_amdgcn_sdot4((int)qc.z, (int)kc.z, d, false);
-    d = __builtin_amdgcn_sdot4((int)qc.w, (int)kc.w, d, false);
-    const float dot = group_sum<LPP>((float)d);
-    if (ok && c == 0) srow[n] = (qs * sk.scales[off / D]) * dot;
+  constexpr int U = kFallbackUnroll, STRIDE = kCsWaves * PPW;
+  for (int n0 = wave * PPW; n0 < vis; n0 += STRIDE * U) {
+    uint4 kc[U];
+    float ks[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * STRIDE + p;
+      const int64_t off = kv_row<D, PAGED>(kv, b, h, n < vis ? n : 0);
+      kc[u] = ld16i8(sk.codes + off + c * 16);
+      ks[u] = sk.scales[off / D];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * STRIDE + p;
+      int d = 0;
+      d = __builtin_amdgcn_sdot4((int)qc.x, (int)kc[u].x, d, false);
+      d = __builtin_amdgcn_sdot4((int)qc.y, (int)kc[u].y, d, false);
+      d = __builtin_amdgcn_sdot4((int)qc.z, (int)kc[u].z, d, false);
+      d = __builtin_amdgcn_sdot4((int)qc.w, (int)kc[u].w, d, false);
+      const float dot = group_sum<LPP>((float)d);
+      if (n < vis && c == 0) srow[n] = (qs * ks[u]) * dot;
+    }
   }
 }
 
