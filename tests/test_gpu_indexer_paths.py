@@ -215,3 +215,33 @@ def test_small_cache_one_workgroup_per_tile(layout):
         if b % 8 == 0:
             want = oracle.row_sparse(q[b, t, hq], K, ocache.values(b, hq // wl.group), idx[b, t, hq], vis)
             check_attn_row(o[b, t, hq], l[b, t, hq], want[0], want[1], f"step row {(b, t, hq)}")
+
+
+def test_fallback_paged_multitoken_ragged():
+    """Planted high keys at the sampled positions of two requests of a ragged, paged, two-token
+    batch push their rows' sampled thresholds above all but the planted keys, so those rows fall
+    short of k candidates and are rescored in full through the page table; every row still gives
+    the exact top-k, and the one-call step selects the same lists and attends to them."""
+    m = _lib()
+    lens = [9000, 40000, 2050, 17777]
+    wl = make_workload(batch=4, q_len=2, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=lens,
+                       k=0.02, layout="paged", page_size=16, max_len=40000, seed=47)
+    for b in (1, 3):  # requests whose rows fall back
+        L = lens[b]
+        stride = -(-L // 1024)  # the sample's stride for a request of length L
+        n = torch.arange(0, L - 2, stride)  # every sampled position: ~250 per query head, far more
+        for hq in range(8):                    # than the ~60 samples the threshold's rank asks for
+            qh = wl.q[b, 1, hq].float()
+            key = (3.0 * qh / qh.norm()).to(torch.bfloat16)
+            sel = n[hq % 4::4]  # a quarter of the sampled positions per query head of the group
+            wl.k_cache[wl.page_table[b, sel // 16].long(), hq // 4, sel % 16] = key
+    idx = _check_indexer(wl)
+    g = wl.to("cuda")
+    o, l, idx_st = m.sparse_decode_step(g.q, cache_of(g), g.k_per_req, k_max=g.k_max, return_indices=True)
+    torch.cuda.synchronize()
+    idx_st = idx_st.cpu().numpy()
+    np.testing.assert_array_equal(idx_st, idx)  # the same selection rule on the same scores
+    o_ref, l_ref = oracle.decode_sparse(bits(wl.q), oracle_cache(wl), idx_st)
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    for r in all_rows(wl):
+        check_attn_row(o[r], l[r], o_ref[r], l_ref[r], f"step row {r}")
