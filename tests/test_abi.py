@@ -307,3 +307,39 @@ def test_sketch_arguments(lib):
     # more candidates need more list room
     assert need < L.topk_index_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 8)
     assert L.topk_index_sketch_workspace_size(ctypes.byref(_shape()), ctypes.byref(_kv()), 10, 0) == 0
+
+
+C_CLIENT = r"""
+#include "ctxsparse.h"
+#include <stdio.h>
+int main(void) {
+  cs_decode_shape s = {2, 1, 8, 2, 128};
+  cs_kv_desc kv = {0};
+  /* a null K pointer: every entry point refuses before any GPU work */
+  cs_status st = topk_index(&s, (const void*)0x10000, &kv, 0.088f, NULL, 10, (int*)0x10000,
+                            (void*)0x10000, 1u << 20, NULL);
+  size_t w = topk_index_workspace_size(&s, &kv, 10);
+  printf("%s %s %d %lu\n", cs_status_str(st), cs_status_str(CS_ERR_SCRATCH_LIMIT), cs_version(),
+         (unsigned long)w);
+  return st == CS_ERR_INVALID_ARG && w == 0 ? 0 : 1;
+}
+"""
+
+
+def test_header_is_c99_and_links_from_c(lib, tmp_path):
+    """include/ctxsparse.h compiles as strict C99 and a C program links against the library and
+    gets the validation statuses through the plain C ABI (no GPU work)."""
+    import shutil
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not installed")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(lib.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                    os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lctxsparse",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.split()[:2] == ["CS_ERR_INVALID_ARG", "CS_ERR_SCRATCH_LIMIT"]
