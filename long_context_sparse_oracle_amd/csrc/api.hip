@@ -237,10 +237,10 @@ TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
 size_t topk_ws(const cs_decode_shape* s, const cs_kv_desc* kv) { return topk_ws_layout(s, kv).total; }
 
 // ---- attention sizing
-// Gather plan: splits per row, entries per split, waves per workgroup (a wave takes
-// kSparseWaveEntries entries per round).
+// Gather plan: splits per row, entries per split, waves per workgroup and the entries a wave
+// takes per round (kSparseWaveEntries, or kSparseWaveEntriesBig for many rows).
 struct SparsePlan {
-  int S, chunk, waves;
+  int S, chunk, waves, entries;
 };
 
 SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
@@ -250,7 +250,10 @@ SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
   // than one round of a workgroup (splitting a one-round list shortens nothing and adds the
   // combine pass).
   const int64_t rows = rows_of(s);
-  const int64_t waves_needed = ceil_div(k_max, cs::kSparseWaveEntries);
+  const int entries = rows >= 2LL * cu_count() && k_max >= cs::kSparseWaves * cs::kSparseWaveEntriesBig
+                          ? cs::kSparseWaveEntriesBig
+                          : cs::kSparseWaveEntries;
+  const int64_t waves_needed = ceil_div(k_max, entries);
   int64_t S;
   if (requested > 0) {
     S = requested;
@@ -267,8 +270,9 @@ SparsePlan sparse_plan(const cs_decode_shape* s, int k_max, int requested) {
   SparsePlan p;
   p.S = (int)ceil_div(k_max, chunk);
   p.chunk = (int)chunk;
-  const int64_t w = ceil_div(chunk, cs::kSparseWaveEntries);
+  const int64_t w = ceil_div(chunk, entries);
   p.waves = (int)(w > cs::kSparseWaves ? cs::kSparseWaves : w);
+  p.entries = entries;
   return p;
 }
 
@@ -404,6 +408,7 @@ cs::AttnLaunch sparse_launch(const cs_decode_shape* shape, const void* q, const 
   a.S = S;
   a.chunk = plan.chunk;
   a.waves = plan.waves;
+  a.entries = plan.entries;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))
@@ -712,6 +717,7 @@ cs_status dense_decode_attn(const cs_decode_shape* shape, const void* q, const c
   a.S = S;
   a.chunk = chunk;
   a.waves = 0;
+  a.entries = 0;
   char* ws = static_cast<char*>(workspace);
   a.part_o = S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_ml = S > 1 ? reinterpret_cast<float*>(ws + align_up((size_t)a.rows * S * a.D * sizeof(float)))

@@ -680,8 +680,9 @@ static hipError_t launch_sparse_t(const AttnLaunch& a, hipStream_t stream) {
   const int items = a.GT * a.S;
   const int64_t blocks = 8LL * ((n_groups + 7) / 8) * items;
   const int waves = a.waves < 1 ? 1 : (a.waves > kSparseWaves ? kSparseWaves : a.waves);
-  hipLaunchKernelGGL((sparse_partial_kernel<D, PAGED, kSparseWaveEntries, kSparseWaves>),
-                     dim3((unsigned)blocks), dim3(waves * kWave), 0, stream, a.q, a.kv, a.indices,
+  auto kern = a.entries == kSparseWaveEntriesBig ? sparse_partial_kernel<D, PAGED, kSparseWaveEntriesBig, kSparseWaves>
+                                                 : sparse_partial_kernel<D, PAGED, kSparseWaveEntries, kSparseWaves>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * kWave), 0, stream, a.q, a.kv, a.indices,
                      a.T, a.Hq, a.G, a.k_max, a.scale_log2, a.S, a.chunk, n_groups, items,
                      a.part_o, a.part_ml, a.out, a.lse);
   return hipGetLastError();

@@ -11,6 +11,10 @@ namespace cs {
 // Sparse attention launch shape: index entries a wave takes per round, and waves per workgroup.
 constexpr int kSparseWaveEntries = 16;
 constexpr int kSparseWaves = 8;
+// With at least twice as many rows as compute units (several workgroups per unit, the gather
+// bandwidth-bound) and lists long enough to give all waves full rounds, a wave takes twice as
+// many entries per round: fewer, longer rounds.
+constexpr int kSparseWaveEntriesBig = 32;
 
 // Positions sampled per (request, KV head) to set the candidate threshold of the filtered indexer;
 // caches of at most this many positions are scored whole and selected in one kernel.
@@ -77,6 +81,7 @@ struct AttnLaunch {
   int k_max;               // sparse only
   int S, chunk;
   int waves;       // sparse only: waves per workgroup
+  int entries;     // sparse only: index entries a wave takes per round
   float* part_o;   // [rows, S, D]
   float* part_ml;  // [rows, S, 2]
   float* out;

@@ -46,6 +46,7 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t) {
   require(a.S >= 1 && a.chunk >= 1 && (int64_t)a.S * a.chunk >= a.k_max, "sparse plan");
   require(a.S == 1 || (a.part_o && a.part_ml), "sparse partials");
   require(a.waves >= 1 && a.waves <= kSparseWaves, "sparse waves");
+  require(a.entries == kSparseWaveEntries || a.entries == kSparseWaveEntriesBig, "sparse entries");
   return hipSuccess;
 }
 hipError_t launch_dense(const AttnLaunch& a, hipStream_t) {
