@@ -116,15 +116,17 @@ void topk_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, i
 
 // Filtered indexer (candidates only) for lists of at most 1/16 of the cache; its score pass
 // runs 4-wave workgroups over chunks of >= 1024 positions, about 16 per compute unit over the
-// call, so ragged lengths still leave the last wave of workgroups short.  With at most half as
-// many tiles as compute units and at most 4 query rows per tile, every candidate workgroup
-// repeats its rows' threshold search (the sample pass is split on both indexers), and about 8
-// longer chunks per unit pay: 3-4% on 16 requests x 8 KV heads at 131072 positions; Qwen-shaped
-// tiles of 8 rows, whose sketch pass keeps the unsplit sample, measured slower with them.
-void cand_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, int* chunks) {
+// call, so ragged lengths still leave the last wave of workgroups short.  When the sample pass is
+// split (at most half as many (request, KV head, 16-row tile) groups as compute units, and on the
+// sketch at most 4 query rows per tile), every candidate workgroup repeats its rows' threshold
+// searches, and longer chunks pay: about 4 per unit on the exact indexer (Qwen-shaped tiles of 8
+// rows at 131072 positions 6% faster, 16 requests x 8 KV heads at 131072 2%, 4 rows at 32768 1%)
+// and 8 on the sketch, whose short candidate workgroups lost 2% at 4 per unit on the last.
+// `sketch` selects the reduced-byte indexer's rule.
+void cand_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, bool sketch, int* chunk, int* chunks) {
   const int64_t groups = (int64_t)s->batch * s->num_kv_heads * ceil_div(gt_of(s), 16);
-  const bool wide = 2 * groups <= cu_count() && gt_of(s) <= 4;
-  const int64_t target = (wide ? 8LL : 16LL) * cu_count();
+  const bool split = 2 * groups <= cu_count() && (!sketch || gt_of(s) <= 4);
+  const int64_t target = (split ? (sketch ? 8LL : 4LL) : 16LL) * cu_count();
   int64_t c = ceil_div(groups * kv->max_len, target);
   c = ceil_div(c, 256) * 256;
   if (c < 1024) c = 1024;
@@ -135,9 +137,9 @@ void cand_chunking(const cs_decode_shape* s, const cs_kv_desc* kv, int* chunk, i
 
 // Per-row pitch (floats) of the score area: the scores of every position, or the candidate slots
 // of the filtered indexer (half a pair per position of every chunk).
-int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv) {
+int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv, bool sketch) {
   int cc, cn;
-  cand_chunking(s, kv, &cc, &cn);
+  cand_chunking(s, kv, sketch, &cc, &cn);
   const int64_t dense = ceil_div(kv->max_len, 64) * 64;
   const int64_t cand = (int64_t)cc * cn;
   return dense > cand ? dense : cand;
@@ -152,7 +154,7 @@ int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv) {
 int64_t cand_lds_keys(const cs_decode_shape* s) { return rows_of(s) <= cu_count() ? 24576 : 12288; }
 
 bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
-  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
+  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv, false) * 4;
   return (int64_t)k_max * 16 <= kv->max_len && (int64_t)k_max * 9 / 2 <= 2 * cand_lds_keys(s) &&
          span < (1LL << 31);
 }
@@ -170,7 +172,7 @@ int64_t sketch_list_stride(const cs_kv_desc* kv, int32_t k_max, int32_t cand_mul
 // The sketch path always runs the candidate pipeline, whose buffer resource spans the score areas
 // of one (request, KV head)'s rows.
 bool sketch_supported(const cs_decode_shape* s, const cs_kv_desc* kv) {
-  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv) * 4;
+  const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv, true) * 4;
   return span < (1LL << 31);
 }
 
@@ -198,11 +200,11 @@ SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_
                           bool step) {
   const size_t rows = (size_t)rows_of(s);
   int cc, cn;
-  cand_chunking(s, kv, &cc, &cn);
+  cand_chunking(s, kv, true, &cc, &cn);
   const size_t ls = (size_t)sketch_list_stride(kv, k_max, cand_mult);
   SketchWs w;
   w.scores = 0;
-  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv, true) * sizeof(float));
   // histograms of the full-score mode, else the sample key prefixes of a split sample pass
   w.counts = w.hist + (sketch_full(s, kv, k_max, cand_mult) ? align_up(rows * 4096 * sizeof(uint32_t))
                                                             : align_up(rows * cs::kTauSamples * sizeof(uint16_t)));
@@ -224,10 +226,10 @@ struct TopkWs {
 TopkWs topk_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv) {
   const size_t rows = (size_t)rows_of(s);
   int cc, cn;
-  cand_chunking(s, kv, &cc, &cn);
+  cand_chunking(s, kv, false, &cc, &cn);
   TopkWs w;
   w.scores = 0;
-  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv) * sizeof(float));
+  w.hist = w.scores + align_up(rows * (size_t)score_stride(s, kv, false) * sizeof(float));
   w.counts = w.hist + align_up(rows * 4096 * sizeof(uint32_t));
   w.tau = w.counts + align_up(rows * (size_t)cn * 4 * sizeof(uint32_t));
   w.total = w.tau + align_up(rows * sizeof(float));
@@ -371,13 +373,13 @@ cs::TopkLaunch topk_launch(const cs_decode_shape* shape, const void* q, const cs
   a.k_per_req = k_per_req;
   a.k_max = k_max;
   topk_chunking(shape, kv, &a.chunk, &a.chunks);
-  cand_chunking(shape, kv, &a.cand_chunk, &a.cand_chunks);
+  cand_chunking(shape, kv, false, &a.cand_chunk, &a.cand_chunks);
   a.filtered = topk_filtered(shape, kv, k_max);
   a.small = kv->max_len <= cs::kTauSamples;  // every position is scored and selected in one kernel
   a.keep_scores = false;
   char* ws = static_cast<char*>(workspace);
   const TopkWs lay = topk_ws_layout(shape, kv);
-  a.score_stride = score_stride(shape, kv);
+  a.score_stride = score_stride(shape, kv, false);
   a.scores = reinterpret_cast<float*>(ws + lay.scores);
   a.hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   a.counts = reinterpret_cast<uint32_t*>(ws + lay.counts);
@@ -456,6 +458,8 @@ cs::TopkLaunch sketch_launch(const cs_decode_shape* shape, const void* q, const 
                              int32_t k_max, int32_t cand_mult, int32_t* indices, char* ws,
                              const SketchWs& lay) {
   cs::TopkLaunch a = topk_launch(shape, q, kv, sm_scale, k_per_req, k_max, indices, ws);
+  cand_chunking(shape, kv, true, &a.cand_chunk, &a.cand_chunks);
+  a.score_stride = score_stride(shape, kv, true);
   a.filtered = true;
   a.small = false;
   a.sketch = true;
