@@ -58,22 +58,17 @@ METRIC = "sparse decode µs/step + gathered-KV GB/s (% HBM peak), speedup vs den
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "ragged_paged_b32_t4"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the launch planning (splits, chunks, kernel variants) decides the traffic as much as the kernels
+_CS = "long_context_sparse_oracle_amd/csrc/"
+_LAUNCH_SOURCES = [_CS + "api.hip", _CS + "launch.h"]
 KERNEL_SOURCES = {
-    "sparse_decode_attn": ["long_context_sparse_oracle_amd/csrc/attention.hip",
-                           "long_context_sparse_oracle_amd/csrc/device_common.h"],
-    "dense_decode_attn": ["long_context_sparse_oracle_amd/csrc/attention.hip",
-                          "long_context_sparse_oracle_amd/csrc/device_common.h"],
-    "topk_index": ["long_context_sparse_oracle_amd/csrc/topk.hip",
-                   "long_context_sparse_oracle_amd/csrc/device_common.h"],
-    "sparse_decode_step": ["long_context_sparse_oracle_amd/csrc/topk.hip",
-                           "long_context_sparse_oracle_amd/csrc/attention.hip",
-                           "long_context_sparse_oracle_amd/csrc/device_common.h"],
-    "topk_index_sketch": ["long_context_sparse_oracle_amd/csrc/topk.hip",
-                          "long_context_sparse_oracle_amd/csrc/sketch.hip",
-                          "long_context_sparse_oracle_amd/csrc/device_common.h"],
-    "sparse_decode_step_sketch": ["long_context_sparse_oracle_amd/csrc/topk.hip",
-                                  "long_context_sparse_oracle_amd/csrc/sketch.hip",
-                                  "long_context_sparse_oracle_amd/csrc/device_common.h"],
+    "sparse_decode_attn": [_CS + "attention.hip", _CS + "device_common.h", *_LAUNCH_SOURCES],
+    "dense_decode_attn": [_CS + "attention.hip", _CS + "device_common.h", *_LAUNCH_SOURCES],
+    "topk_index": [_CS + "topk.hip", _CS + "device_common.h", *_LAUNCH_SOURCES],
+    "sparse_decode_step": [_CS + "topk.hip", _CS + "attention.hip", _CS + "device_common.h", *_LAUNCH_SOURCES],
+    "topk_index_sketch": [_CS + "topk.hip", _CS + "sketch.hip", _CS + "device_common.h", *_LAUNCH_SOURCES],
+    "sparse_decode_step_sketch": [_CS + "topk.hip", _CS + "sketch.hip", _CS + "device_common.h",
+                                  *_LAUNCH_SOURCES],
 }
 
 
