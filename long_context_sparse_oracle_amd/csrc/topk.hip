@@ -208,8 +208,9 @@ __global__ __launch_bounds__(kScoreMaxThreads) void score_hist_kernel(
 }
 
 // ============================================================================ select
-// Block-wide exclusive prefix sum over the NW * 64 threads' values.
-template <int NW = kSelWaves>
+// Block-wide exclusive prefix sum over the NW * 64 threads' values.  SYNC_AFTER = false leaves
+// out the closing barrier, for callers that pass another barrier before wsum is written again.
+template <int NW = kSelWaves, bool SYNC_AFTER = true>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan_u32(v);
@@ -223,7 +224,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     all += t;
   }
   if (total) *total = all;
-  __syncthreads();  // wsum may be reused right away
+  if constexpr (SYNC_AFTER) __syncthreads();  // wsum may be reused right away
   return before + x - v;
 }
 
@@ -265,7 +266,7 @@ __device__ uint32_t find_threshold(const uint32_t* hist, int nbins, uint32_t nee
   }
   if (threadIdx.x == 0) sh.found = 0u;
   uint32_t total;
-  uint32_t above = block_excl_scan<NW>(sum, sh.wsum, &total);
+  uint32_t above = block_excl_scan<NW, false>(sum, sh.wsum, &total);  // the barrier below closes it
   if (above < need && above + sum >= need) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // suggest (the writes interleave with the K stream), so for k <= N/16 the indexer avoids them:
 //  A. sample_tau_kernel scores a strided sample of at most kTauSamples positions per (request,
 //     KV head) and sets, per row, a threshold tau: the 16-bit key prefix of the sample's r-th
-//     largest score, r ~ kCandFactor * k * (samples / visible);
+//     largest score, r from cand_rank (about 2.5 k samples / visible at 50x sparsity);
 //  B. score_cand_kernel then scores
 //     every position once, as score_hist_kernel does, and keeps only the candidates s >= tau as
 //     (position, score) pairs, staged in LDS and written a 128-byte line at a time into per-wave
@@ -584,7 +585,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //     largest score is >= tau, so every position of the top-k is a candidate) and no slot
 //     overflowed; otherwise the workgroup recomputes every score of its row and selects from
 //     those (exact, slow, rare).
-constexpr int kCandFactor = 3;
+// The rank r of the threshold among a row's ns_row samples.  About mu = kk * ns_row / vis samples
+// fall among the row's kk largest scores; when r or more do, fewer than kk positions reach tau and
+// the row falls back.  r = ceil(mu + 4.8 sqrt(mu) + 9.5) keeps that chance below 1e-8 per row for
+// every mu (binomial upper tail, 1024 samples of i.i.d. scores) with as few candidates as that
+// allows: their lines are the indexer's only writes and cost about 1 TB/s against the K stream.
+// It matches 2.5 mu at 50x sparsity (r = 52); a fixed 3 mu with a minimum of 32 measured 2% slower
+// on the indexer and 6% on the sketch step at 50x, and wrote more lines than needed at 10x
+// (3 mu = 308 where 160 suffice) and 1000x (32 where 16 suffice).
+__host__ __device__ inline int64_t cand_rank(int64_t kk, int64_t ns_row, int64_t vis) {
+  const float mu = (float)kk * (float)ns_row / (float)vis;
+  return (int64_t)ceilf(mu + 4.8f * sqrtf(mu) + 9.5f);
+}
 
 // Sampling stride of a request of length L: every stride-th position, at most kTauSamples.
 __device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L + kTauSamples - 1) / kTauSamples : 1; }
@@ -598,12 +610,9 @@ constexpr int kCandWaves = 4;
 __host__ __device__ constexpr int cand_cap(int chunk) { return chunk / (2 * kCandWaves); }
 
 // tau of one row from its sample keys (one wave): the largest 16-bit prefix P with at least r
-// keys >= P << 16, r = max(ceil(kCandFactor * kk * samples_visible / vis), kMinRank); -inf when
-// every visible position has to be a candidate, +inf when the selection needs none (k = 0 or
-// k >= visible).  The fraction of the row scoring >= tau then has mean about r / samples and
-// relative spread about 1 / sqrt(r); kMinRank keeps that spread small for very sparse k (where
-// the kCandFactor rule alone would put r at a handful of samples).
-constexpr int kMinRank = 32;
+// keys >= P << 16, r = cand_rank(kk, samples_visible, vis); -inf when every visible position has
+// to be a candidate, +inf when the selection needs none (k = 0 or k >= visible).  The fraction of
+// the row scoring >= tau then has mean about r / samples and relative spread about 1 / sqrt(r).
 
 // The search for P on the 16-bit key prefixes of NR rows' samples, 16 per lane and row in any
 // order (0 for a sample the row does not see), for ranks rr; the rows' searches are interleaved
@@ -637,8 +646,7 @@ __device__ __forceinline__ int tau_rank(int vis, int kk, int stride, float* spec
     return 0;
   }
   const int ns_row = (vis + stride - 1) / stride;
-  int64_t rr = ((int64_t)kCandFactor * kk * ns_row + vis - 1) / vis;
-  if (rr < kMinRank) rr = kMinRank;
+  const int64_t rr = cand_rank(kk, ns_row, vis);
   if (rr >= ns_row) {
     *special = -INFINITY;
     return 0;
@@ -1236,7 +1244,9 @@ constexpr int kCsBlocks = 3;
 constexpr int kCsBlocksBig = 6;
 
 // Finds the kk-th largest key of the list (kmin <= every key <= kmax) by radix select over the
-// bits below their common prefix, in digits of up to 11 bits; hist holds 2048 counters.
+// bits below their common prefix, in digits of up to 11 bits.  hist holds two areas of 2048
+// counters used in turn: the next digit's area is cleared while this digit is counted, so a digit
+// costs three barriers (after the counts, and the two of find_threshold).
 // Returns the key and sets need (items equal to it that are taken) and cnt_eq (items equal to it).
 template <class KeyAt>
 __device__ uint32_t radix_kth(KeyAt key_at, int total, int kk, uint32_t kmin, uint32_t kmax,
@@ -1247,25 +1257,33 @@ __device__ uint32_t radix_kth(KeyAt key_at, int total, int kk, uint32_t kmin, ui
   if (kmin == kmax) return kmin;  // one key value
   int lo = 32 - __clz(kmin ^ kmax);  // bits [0, lo) vary
   uint32_t prefix = lo >= 32 ? 0u : kmin >> lo;
+  for (int i = tid; i < 2048; i += kCsThreads) hist[i] = 0u;
+  __syncthreads();
+  int area = 0;
   while (lo > 0) {
     const int width = lo >= 11 ? 11 : lo;
     const int shift = lo - width;
     const int nb = 1 << width;
-    for (int i = tid; i < nb; i += kCsThreads) hist[i] = 0u;
-    __syncthreads();
+    uint32_t* h = hist + area * 2048;
+    // the other area was last read by the previous digit's find_threshold, which ended in a barrier
+    if (shift > 0) {
+      uint32_t* next = hist + (area ^ 1) * 2048;
+      for (int i = tid; i < 2048; i += kCsThreads) next[i] = 0u;
+    }
     for (int f = tid; f < total; f += kCsThreads) {
       const uint32_t key = key_at(f);
-      if (lo >= 32 || (key >> lo) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      if (lo >= 32 || (key >> lo) == prefix) atomicAdd(&h[(key >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    for (int i = nb + tid; i < 2048; i += kCsThreads) hist[i] = 0u;  // bins above nb count nothing
-    __syncthreads();
-    find_threshold<2048 / kCsThreads, kCsWaves>(hist, 2048, need, sh);
+    // bins at and above nb count nothing: they were cleared and no key maps there
+    find_threshold<2048 / kCsThreads, kCsWaves>(h, 2048, need, sh);
+    // sh.thr_* are read here, before this thread reaches the next digit's first barrier, and
+    // written again only after it
     prefix = (prefix << width) | sh.thr_bin;
     need -= sh.thr_above;
     cnt_eq = sh.thr_count;
     lo = shift;
-    __syncthreads();
+    area ^= 1;
   }
   return prefix;
 }
@@ -1285,11 +1303,14 @@ __device__ __forceinline__ void emit_block(int fb, int total, const uint32_t (&k
                                            const uint32_t (&pos)[kCsPer], uint32_t kstar, uint32_t need,
                                            bool take_all_eq, uint32_t& eq_base, uint32_t& out_base,
                                            const SelOut& so, SelShared& sh) {
-  uint32_t eqc = 0;
+  uint32_t eq_tot = 0, sel_tot;
+  uint32_t eq_rank = eq_base;
+  if (!take_all_eq) {  // workgroup-uniform: the ranks among keys equal to kstar decide
+    uint32_t eqc = 0;
 #pragma unroll
-  for (int e = 0; e < kCsPer; ++e) eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
-  uint32_t eq_tot, sel_tot;
-  uint32_t eq_rank = eq_base + block_excl_scan<kCsWaves>(eqc, sh.wsum, &eq_tot);
+    for (int e = 0; e < kCsPer; ++e) eqc += (fb + e < total && keys[e] == kstar) ? 1u : 0u;
+    eq_rank += block_excl_scan<kCsWaves>(eqc, sh.wsum, &eq_tot);
+  }
   uint32_t selc = 0, selm = 0;
 #pragma unroll
   for (int e = 0; e < kCsPer; ++e) {
@@ -1463,22 +1484,29 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
     sh.kmax = 0u;
   }
   __syncthreads();
+  // every block's loads are issued before any is used
+  const int nblk = ((int)total + kCsThreads * kCsPer - 1) / (kCsThreads * kCsPer);  // <= MB
   uint32_t preg[MB][kCsPer];
+  uint2 pr[MB][kCsPer];
+#pragma unroll
+  for (int blk = 0; blk < MB; ++blk) {
+    if (blk < nblk) {
+      int64_t off[kCsPer];
+      src.offsets(blk * kCsThreads * kCsPer + tid * kCsPer, (int)total, off);
+#pragma unroll
+      for (int e = 0; e < kCsPer; ++e) pr[blk][e] = src.base[off[e]];
+    }
+  }
   uint32_t lmin = 0xffffffffu, lmax = 0u;
 #pragma unroll
   for (int blk = 0; blk < MB; ++blk) {
+    if (blk >= nblk) break;
     const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
-    if (blk * kCsThreads * kCsPer >= (int)total) break;
-    int64_t off[kCsPer];
-    src.offsets(fb, (int)total, off);
-    uint2 pr[kCsPer];
-#pragma unroll
-    for (int e = 0; e < kCsPer; ++e) pr[e] = src.base[off[e]];
 #pragma unroll
     for (int e = 0; e < kCsPer; ++e) {
-      preg[blk][e] = pr[e].x;
+      preg[blk][e] = pr[blk][e].x;
       if (fb + e < (int)total) {
-        const uint32_t key = ord_key(__uint_as_float(pr[e].y));
+        const uint32_t key = ord_key(__uint_as_float(pr[blk][e].y));
         lds_key[fb + e] = key;
         lmin = min(lmin, key);
         lmax = max(lmax, key);
@@ -1546,7 +1574,7 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     const uint32_t* __restrict__ counts, int chunk, int chunks, int k_max, int lds_cap,
     int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
     float* __restrict__ out, float* __restrict__ lse, int B) {
-  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
+  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2 x 2048 histogram counters
   __shared__ SelShared sh;
   __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
   uint32_t* lds_key = smem;
@@ -1766,7 +1794,7 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
     int32_t* __restrict__ list_pos, float* __restrict__ list_score, int list_stride, bool listed,
     int32_t* __restrict__ indices, int32_t* __restrict__ sel_pos, float* __restrict__ sel_score,
     float* __restrict__ out, float* __restrict__ lse, int B) {
-  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2048 histogram counters
+  extern __shared__ uint32_t smem[];  // lds_cap candidate keys, then 2 x 2048 histogram counters
   __shared__ SelShared sh;
   __shared__ uint32_t prefix_s[kMaxCandSlots + 1];
   uint32_t* lds_key = smem;
@@ -1951,15 +1979,19 @@ static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
                        a.score_stride, a.counts, a.cand_chunk, a.cand_chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // candidate keys held in LDS: about kCandFactor * (entries kept) expected, room for 4.5 times
-  // the largest list, at most kCsBlocks * kCsThreads * kCsPer = 12288; when there are no more rows
-  // than compute units (one workgroup per unit anyway), up to twice that
+  // candidate keys held in LDS: 1.6 times the count expected at the longest row (cand_rank of
+  // its samples), at least twice the largest list, at most kCsBlocks * kCsThreads * kCsPer = 12288;
+  // when there are no more rows than compute units (one workgroup per unit anyway), up to twice
+  // that.  Rows with more candidates select from the slots in global memory.
   const int64_t keep_max = SK ? (int64_t)a.list_stride : (int64_t)a.k_max;
-  int lds_cap = (int)((keep_max * 9 / 2 + 255) / 256 * 256);
+  const int64_t ns_max = a.kv.max_len < kTauSamples ? a.kv.max_len : kTauSamples;
+  const int64_t expect = cand_rank(keep_max, ns_max, a.kv.max_len) * a.kv.max_len / ns_max;
+  const int64_t want = expect * 8 / 5 > 2 * keep_max ? expect * 8 / 5 : 2 * keep_max;
+  int lds_cap = (int)((min(want, (int64_t)kCsBlocksBig * kCsThreads * kCsPer) + 255) / 256 * 256);
   const bool big = lds_cap > kCsBlocks * kCsThreads * kCsPer && a.rows <= a.cus;
   const int cap_max = (big ? kCsBlocksBig : kCsBlocks) * kCsThreads * kCsPer;
   if (lds_cap > cap_max) lds_cap = cap_max;
-  const size_t lds = ((size_t)lds_cap + 2048) * sizeof(uint32_t);
+  const size_t lds = ((size_t)lds_cap + 4096) * sizeof(uint32_t);  // keys, two histogram areas
   if constexpr (SK) {
     auto sel = a.fused ? (big ? sketch_select_kernel<D, PAGED, true, kCsBlocksBig> : sketch_select_kernel<D, PAGED, true, kCsBlocks>)
                        : (big ? sketch_select_kernel<D, PAGED, false, kCsBlocksBig> : sketch_select_kernel<D, PAGED, false, kCsBlocks>);
