@@ -100,3 +100,16 @@ def check_attn_row(o, lse, want_o, want_lse, where=""):
 
 def all_rows(wl):
     return [(b, t, h) for b in range(wl.batch) for t in range(wl.q_len) for h in range(wl.num_q_heads)]
+
+
+def threshold_regimes_workload():
+    # k_max = 4096 = max_len / 16 keeps every row on the filtered path.  Expected samples among a
+    # row's top k, mu = k * samples / visible: about 0.06, 10 and 64 for the three full rows
+    # (threshold ranks 11, 36 and 112 of 1024); about 400 for the 8000-position row, whose
+    # threshold keeps about half its positions so that slots overflow and it is recomputed in
+    # full; and past the sample count for the two short rows (every position a candidate).
+    from workloads import make_workload
+
+    return make_workload(batch=6, q_len=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         seq_lens=[65536, 65536, 65536, 8000, 3000, 1500],
+                         k=[4, 655, 4096, 3200, 2900, 1499], max_len=65536, needles_per_head=2, seed=49)

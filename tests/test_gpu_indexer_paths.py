@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from tests._util import bits, oracle_cache
-from tests.gpu_util import all_rows, cache_of, check_attn_row, check_topk_row
+from tests.gpu_util import all_rows, cache_of, check_attn_row, check_topk_row, threshold_regimes_workload
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -65,6 +65,11 @@ def test_threshold_path_many_rows_gqa():
     wl = make_workload(batch=2, q_len=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
                        seq_lens=[40000, 23457], k=0.02, max_len=40003, needles_per_head=4, seed=42)
     _check_indexer(wl)
+
+
+def test_threshold_rule_regimes():
+    """The candidate threshold's rank across its regimes, on the index-only indexer."""
+    _check_indexer(threshold_regimes_workload())
 
 
 @pytest.mark.parametrize("k,label", [(256, "filtered at k = N/16"), (257, "full-score path")])

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from tests._util import bits, oracle_cache
-from tests.gpu_util import all_rows, cache_of, check_attn_row, check_sketch_row, logical_kv
+from tests.gpu_util import all_rows, cache_of, check_attn_row, check_sketch_row, logical_kv, threshold_regimes_workload
 from workloads import make_named, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -115,6 +115,14 @@ def test_sketch_indexer_gqa_ragged_tail():
     wl = make_workload(batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
                        seq_lens=[20000, 7777], k=0.02, max_len=20003, needles_per_head=3, seed=63)
     _run(wl, m=2)
+
+
+@pytest.mark.parametrize("step", [False, True])
+def test_sketch_threshold_rule_regimes(step):
+    """cand_mult 1 keeps m * k_max = max_len / 16 on the sketch's candidate path: the sketch
+    threshold's rank across its regimes (very sparse rows, a row recomputed after its slots
+    overflow, rows where every position is a candidate), index-only and as the one-call step."""
+    _run(threshold_regimes_workload(), m=1, step=step)
 
 
 @pytest.mark.parametrize("m", [1, 3])

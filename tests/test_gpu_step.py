@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from tests._util import bits, oracle_cache
-from tests.gpu_util import all_rows, cache_of, check_attn_row, check_topk_row
+from tests.gpu_util import all_rows, cache_of, check_attn_row, check_topk_row, threshold_regimes_workload
 from workloads import make_named, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +46,13 @@ def _check_step(wl_cpu, k_max=None, rows=None):
         check_topk_row(idx[b, t, hq], q[b, t, hq], K, vis, min(int(kreq[b]), kmax), f"row {(b, t, hq)}")
         want = oracle.row_sparse(q[b, t, hq], K, V, idx[b, t, hq], vis)
         check_attn_row(out[b, t, hq], lse[b, t, hq], want[0], want[1], f"step row {(b, t, hq)}")
+
+
+def test_step_threshold_rule_regimes():
+    """The one-call step over the same rows as the indexer's threshold-regime test: very sparse
+    rows, a row recomputed in full after its slots overflow, rows where every position is a
+    candidate."""
+    _check_step(threshold_regimes_workload())
 
 
 def test_step_fused_gqa_ragged_tail():
