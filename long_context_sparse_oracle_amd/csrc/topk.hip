@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //     largest score, r from cand_rank (about 2.5 k samples / visible at 50x sparsity);
 //  B. score_cand_kernel then scores
 //     every position once, as score_hist_kernel does, and keeps only the candidates s >= tau as
-//     (position, score) pairs, staged in LDS and written a 128-byte line at a time into per-wave
+//     (score, position) entries, staged in LDS and written a 128-byte line at a time into per-wave
 //     slots of the workspace.  A wave scans one contiguous range, so the slots concatenated in
 //     (chunk, wave) order list a row's candidates in ascending position order;
 //  C. cand_select_kernel selects the k largest candidates by radix select and writes them in that
@@ -603,11 +603,28 @@ __device__ __forceinline__ int tau_stride(int L) { return L > kTauSamples ? (L +
 
 // Candidate slots: wave w of workgroup (chunk c) of row `row` scans the positions
 // [c * chunk + w * chunk / kCandWaves, + chunk / kCandWaves) and owns slot s = c * kCandWaves + w
-// of the row's workspace area: up to cand_cap(chunk) (position, score) pairs, stored as 16-pair
-// lines interleaved across the row's nsub = chunks * kCandWaves slots -- line l of slot s is line
-// l * nsub + s of the area -- so the first lines of all slots, the ones most written, lie together.
+// of the row's workspace area: up to cand_cap(chunk) candidates in 128-byte lines of
+// kLinePairs = 20 -- words 0..19 their float32 scores, words 20..29 their positions as 16-bit
+// offsets from the slot's first position (a slot spans at most 4096), words 30..31 unused; 20
+// candidates in 128 bytes instead of 16 (position, score) pairs, since these lines are the
+// indexer's only writes and cost far more per byte than the K stream (measured: 1-2% faster
+// indexer calls, less than the bytes suggested).  Lines are interleaved
+// across the row's nsub = chunks * kCandWaves slots -- line l of slot s is line l * nsub + s of
+// the area -- so the first lines of all slots, the ones most written, lie together.
 constexpr int kCandWaves = 4;
-__host__ __device__ constexpr int cand_cap(int chunk) { return chunk / (2 * kCandWaves); }
+constexpr int kLinePairs = 20;
+
+// Byte offset, in a staging ring of 2 * kLinePairs entries (scores, then 16-bit offsets), of 8-byte
+// part p (0..15) of the line whose first entry is hd (0 or kLinePairs): parts 0..9 hold scores
+// hd + 2p, hd + 2p + 1; parts 10..14 offsets hd + 4 (p - 10) .. + 3; part 15 is unused and reads
+// the last four offsets of the line again.
+__device__ __forceinline__ uint32_t line_part_8(uint32_t hd, uint32_t p) {
+  constexpr uint32_t kOffsets = 2 * kLinePairs * 4;  // byte offset of the ring's 16-bit offsets
+  return p < 10u ? (hd + 2u * p) * 4u : kOffsets + (hd + 4u * (p < 15u ? p - 10u : 4u)) * 2u;
+}
+__host__ __device__ constexpr int cand_cap(int chunk) {
+  return chunk / (2 * kCandWaves) / kLinePairs * kLinePairs;
+}
 
 // tau of one row from its sample keys (one wave): the largest 16-bit prefix P with at least r
 // keys >= P << 16, r = cand_rank(kk, samples_visible, vis); -inf when every visible position has
@@ -940,7 +957,10 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
     const int32_t* __restrict__ k_per_req, int k_max, int cand_mult, float* __restrict__ region,
     int64_t score_stride, uint32_t* __restrict__ counts, int chunk, int chunks) {
   extern __shared__ int lds_pages[];
-  __shared__ __align__(16) uint2 stage[kCandWaves][16][32];  // per wave and row: ring of staged candidates
+  // per wave and row: a ring of kRing staged candidates, their scores (4 bytes each) then their
+  // slot offsets (2 bytes each), so that a line's 20 scores and 20 offsets lie together
+  constexpr int kRing = 2 * kLinePairs;
+  __shared__ __align__(16) unsigned char stage[kCandWaves][16][kRing * 6];
   __shared__ float tau_sh[16];                                 // PREFIX: the tile's thresholds
   constexpr int KS = SK ? D / 64 : D / 32;  // 16-byte operand steps per lane
   constexpr int UNR = kScoreUnroll;  // tiles per step (twice as many for the sketch measured no faster)
@@ -1108,26 +1128,31 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       const bool in_range = n < wend;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        uint2* st = stage[wave][4 * i + g4];
+        unsigned char* st = stage[wave][4 * i + g4];
         const float s = sc[i];
         const bool pred = in_range && n < vis[i] && s >= th[i];
         const uint64_t mask = __ballot(pred);
         const uint32_t seg = (uint32_t)(mask >> (16 * g4)) & 0xffffu;
-        if (pred) st[(head[i] + fill[i] + __popc(seg & ((1u << m) - 1u))) & 31u] =
-            make_uint2((uint32_t)n, __float_as_uint(s));
+        if (pred) {
+          // head + fill <= 39 and the rank < 16: one wrap at most
+          uint32_t e = head[i] + fill[i] + __popc(seg & ((1u << m) - 1u));
+          e = e >= (uint32_t)kRing ? e - kRing : e;
+          *reinterpret_cast<float*>(st + e * 4) = s;
+          *reinterpret_cast<uint16_t*>(st + kRing * 4 + e * 2) = (uint16_t)(n - wbeg);
+        }
         fill[i] += __popc(seg);
         if constexpr (NI == 1) {
           wave_lds_fence();
-          const uint2 v = st[(head[i] + m) & 31u];
-          const bool full = fill[i] >= 16u;
-          const bool write = full && valid[i] && done[i] + 16u <= (uint32_t)cap;
+          const uint2 v = *reinterpret_cast<const uint2*>(st + line_part_8(head[i], (uint32_t)m));
+          const bool full = fill[i] >= (uint32_t)kLinePairs;
+          const bool write = full && valid[i] && done[i] + kLinePairs <= (uint32_t)cap;
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
-                                                (int)(write ? slot[i] + (done[i] / 16u) * line_stride + m * 8u : kDrop), 0, 0);
+                                                (int)(write ? slot[i] + (done[i] / kLinePairs) * line_stride + m * 8u : kDrop), 0, 0);
         }
       }
       if constexpr (NI >= 2) {
         // rows 4 i + g4 and 4 (i + 1) + g4 share one 16-byte store per lane: lanes 8 h .. 8 h + 7
-        // of lane group g4 write the line of row 4 (i + h) + g4, two pairs each
+        // of lane group g4 write the line of row 4 (i + h) + g4, 16 bytes (two 8-byte parts) each
         wave_lds_fence();
         const uint32_t h = (uint32_t)(m >> 3) & 1u, j = (uint32_t)m & 7u;
 #pragma unroll
@@ -1137,18 +1162,21 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
           const uint32_t dn = h ? done[i + 1] : done[i];
           const uint32_t sl = h ? slot[i + 1] : slot[i];
           const bool vd = h ? valid[i + 1] : valid[i];
-          const uint4 v = *reinterpret_cast<const uint4*>(&stage[wave][4 * (i + (int)h) + g4][(hd + 2u * j) & 31u]);
-          const bool write = fl >= 16u && vd && dn + 16u <= (uint32_t)cap;
+          const unsigned char* st = stage[wave][4 * (i + (int)h) + g4];
+          const uint2 lo = *reinterpret_cast<const uint2*>(st + line_part_8(hd, 2u * j));
+          const uint2 hi = *reinterpret_cast<const uint2*>(st + line_part_8(hd, 2u * j + 1u));
+          const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const bool write = fl >= (uint32_t)kLinePairs && vd && dn + kLinePairs <= (uint32_t)cap;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), out_rsrc,
-                                                 (int)(write ? sl + (dn / 16u) * line_stride + j * 16u : kDrop), 0, 0);
+                                                 (int)(write ? sl + (dn / kLinePairs) * line_stride + j * 16u : kDrop), 0, 0);
         }
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const bool full = fill[i] >= 16u;
-        head[i] = full ? (head[i] + 16u) & 31u : head[i];
-        done[i] += full ? 16u : 0u;
-        fill[i] -= full ? 16u : 0u;
+        const bool full = fill[i] >= (uint32_t)kLinePairs;
+        head[i] = full ? (uint32_t)kLinePairs - head[i] : head[i];  // 0 <-> 20
+        done[i] += full ? (uint32_t)kLinePairs : 0u;
+        fill[i] -= full ? (uint32_t)kLinePairs : 0u;
       }
     }
   };
@@ -1163,13 +1191,14 @@ __global__ __launch_bounds__(kCandWaves * kWave) void score_cand_kernel(
       n0 += 2 * kStep;
     } while (n0 < wend);
   }
+  // the last, partial line of each row (its count says how many entries are valid)
   wave_lds_fence();
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint2 v = stage[wave][4 * i + g4][(head[i] + m) & 31u];
-    const bool write = valid[i] && (uint32_t)m < fill[i] && done[i] + m < (uint32_t)cap;
+    const uint2 v = *reinterpret_cast<const uint2*>(stage[wave][4 * i + g4] + line_part_8(head[i], (uint32_t)m));
+    const bool write = valid[i] && fill[i] > 0u && done[i] < (uint32_t)cap;
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, v), out_rsrc,
-                                          (int)(write ? slot[i] + ((done[i] + m) / 16u) * line_stride + ((done[i] + m) & 15u) * 8u : kDrop), 0, 0);
+                                          (int)(write ? slot[i] + (done[i] / kLinePairs) * line_stride + m * 8u : kDrop), 0, 0);
     if (valid[i] && m == 0) counts[(grow[i] * chunks + c) * kCandWaves + wave] = done[i] + fill[i];
   }
 }
@@ -1182,16 +1211,18 @@ constexpr int kCsPer = 8;  // consecutive items per thread in the ordered passes
 constexpr int kFallbackUnroll = 8;  // key rows per lane group in flight when a row is rescored whole
 
 // Candidates of a row in position order, from the slots: item f lives in the slot s with
-// prefix[s] <= f < prefix[s + 1].  Keys come from LDS when lds_key is set.
+// prefix[s] <= f < prefix[s + 1], as entry j = f - prefix[s] of it.  Keys come from LDS when
+// lds_key is set.
 struct CandSource {
-  const uint2* base;       // the row's slot area
+  const uint32_t* base;    // the row's slot area, as 32-bit words
   const uint32_t* prefix;  // [nsub + 1] exclusive prefix of the slot counts (LDS)
   int nsub, cap;
   int nsub_all;            // slots of a row (chunks * kCandWaves): the line interleave
+  int span;                // positions per slot (chunk / kCandWaves): slot s starts at s * span
   const uint32_t* lds_key;
-  // pair index of entry j of slot sl (16-pair lines interleaved across the nsub_all slots)
-  __device__ __forceinline__ int64_t pair_of(int sl, int j) const {
-    return ((int64_t)(j >> 4) * nsub_all + sl) * 16 + (j & 15);
+  // first word of the line holding entry j of slot sl (lines interleaved across nsub_all slots)
+  __device__ __forceinline__ int64_t line_word(int sl, int j) const {
+    return ((int64_t)(j / kLinePairs) * nsub_all + sl) * 32;
   }
   __device__ __forceinline__ int slot_of(int f) const {
     int lo = 0, hi = nsub - 1;
@@ -1201,30 +1232,41 @@ struct CandSource {
     }
     return lo;
   }
-  // pair offsets of items f0 .. f0 + kCsPer - 1 (the valid ones, f < total)
-  __device__ __forceinline__ void offsets(int f0, int total, int64_t (&off)[kCsPer]) const {
+  // items f0 .. f0 + kCsPer - 1 (the valid ones, f < total; others 0): the word index of each
+  // score, the 16-bit index of each offset and the first position of each slot
+  __device__ __forceinline__ void locate(int f0, int total, int64_t (&sw)[kCsPer], int64_t (&ow)[kCsPer],
+                                         int (&first)[kCsPer]) const {
     int sl = f0 < total ? slot_of(f0) : 0;
 #pragma unroll
     for (int e = 0; e < kCsPer; ++e) {
       const int f = f0 + e;
       if (f < total) {
         while ((int)prefix[sl + 1] <= f) ++sl;
-        off[e] = pair_of(sl, f - (int)prefix[sl]);
+        const int j = f - (int)prefix[sl];
+        const int64_t lw = line_word(sl, j);
+        sw[e] = lw + j % kLinePairs;
+        ow[e] = (lw + kLinePairs) * 2 + j % kLinePairs;
+        first[e] = sl * span;
       } else {
-        off[e] = 0;
+        sw[e] = 0;
+        ow[e] = 0;
+        first[e] = 0;
       }
     }
   }
   __device__ __forceinline__ uint32_t key(int f) const {
     if (lds_key) return lds_key[f];
     const int sl = slot_of(f);
-    return ord_key(__uint_as_float(base[pair_of(sl, f - (int)prefix[sl])].y));
+    const int j = f - (int)prefix[sl];
+    return ord_key(__uint_as_float(base[line_word(sl, j) + j % kLinePairs]));
   }
   __device__ __forceinline__ void pos8(int f0, int total, uint32_t sel, uint32_t (&p)[kCsPer]) const {
-    int64_t off[kCsPer];
-    offsets(f0, total, off);
+    int64_t sw[kCsPer], ow[kCsPer];
+    int first[kCsPer];
+    locate(f0, total, sw, ow, first);
+    const uint16_t* off16 = reinterpret_cast<const uint16_t*>(base);
 #pragma unroll
-    for (int e = 0; e < kCsPer; ++e) p[e] = ((sel >> e) & 1u) ? base[off[e]].x : 0u;
+    for (int e = 0; e < kCsPer; ++e) p[e] = ((sel >> e) & 1u) ? (uint32_t)first[e] + off16[ow[e]] : 0u;
   }
 };
 
@@ -1462,16 +1504,17 @@ __device__ void attend_list(const KVArgs& kv, int b, int h, const int32_t* __res
 // lds_cap <= MB * kCsThreads * kCsPer of them).
 template <int MB>
 __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, int kk, int k_max,
-                          int row, float* __restrict__ region, int64_t score_stride, int chunks,
+                          int row, float* __restrict__ region, int64_t score_stride, int chunk, int chunks,
                           const uint32_t* prefix_s, uint32_t* lds_key, int lds_cap, uint32_t* hist,
                           SelShared& sh) {
   const int tid = threadIdx.x;
   CandSource src;
-  src.base = reinterpret_cast<const uint2*>(region + (int64_t)row * score_stride);
+  src.base = reinterpret_cast<const uint32_t*>(region + (int64_t)row * score_stride);
   src.prefix = prefix_s;
   src.nsub = nsub;
   src.cap = cap;
   src.nsub_all = chunks * kCandWaves;
+  src.span = chunk / kCandWaves;
   src.lds_key = nullptr;
   if (total > (uint32_t)lds_cap) {  // too many to hold: every pass reads the slots
     select_ordered(src, (int)total, kk, k_max, so, hist, sh);
@@ -1486,15 +1529,21 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
   __syncthreads();
   // every block's loads are issued before any is used
   const int nblk = ((int)total + kCsThreads * kCsPer - 1) / (kCsThreads * kCsPer);  // <= MB
-  uint32_t preg[MB][kCsPer];
-  uint2 pr[MB][kCsPer];
+  uint32_t preg[MB][kCsPer];  // the slot's first position, then the item's position
+  uint32_t sc[MB][kCsPer], of[MB][kCsPer];
+  const uint16_t* off16 = reinterpret_cast<const uint16_t*>(src.base);
 #pragma unroll
   for (int blk = 0; blk < MB; ++blk) {
     if (blk < nblk) {
-      int64_t off[kCsPer];
-      src.offsets(blk * kCsThreads * kCsPer + tid * kCsPer, (int)total, off);
+      int64_t sw[kCsPer], ow[kCsPer];
+      int first[kCsPer];
+      src.locate(blk * kCsThreads * kCsPer + tid * kCsPer, (int)total, sw, ow, first);
 #pragma unroll
-      for (int e = 0; e < kCsPer; ++e) pr[blk][e] = src.base[off[e]];
+      for (int e = 0; e < kCsPer; ++e) {
+        sc[blk][e] = src.base[sw[e]];
+        of[blk][e] = off16[ow[e]];
+        preg[blk][e] = (uint32_t)first[e];
+      }
     }
   }
   uint32_t lmin = 0xffffffffu, lmax = 0u;
@@ -1504,9 +1553,9 @@ __device__ void cand_path(uint32_t total, int nsub, int cap, const SelOut& so, i
     const int fb = blk * kCsThreads * kCsPer + tid * kCsPer;
 #pragma unroll
     for (int e = 0; e < kCsPer; ++e) {
-      preg[blk][e] = pr[blk][e].x;
+      preg[blk][e] += of[blk][e];
       if (fb + e < (int)total) {
-        const uint32_t key = ord_key(__uint_as_float(pr[blk][e].y));
+        const uint32_t key = ord_key(__uint_as_float(sc[blk][e]));
         lds_key[fb + e] = key;
         lmin = min(lmin, key);
         lmax = max(lmax, key);
@@ -1644,7 +1693,7 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
     __syncthreads();
     select_ordered(DenseSource{srow}, vis, kk, k_max, so, hist, sh);
   } else {
-    cand_path<MB>(total, nsub, cap, so, kk, k_max, row, region, score_stride, chunks, prefix_s, lds_key,
+    cand_path<MB>(total, nsub, cap, so, kk, k_max, row, region, score_stride, chunk, chunks, prefix_s, lds_key,
               lds_cap, hist, sh);
   }
   if constexpr (FUSED) {
@@ -1850,7 +1899,7 @@ __global__ __launch_bounds__(kCsThreads) void sketch_select_kernel(
       __syncthreads();
       select_ordered(DenseSource{srow}, vis, nc, lk, lo, hist, sh);
     } else {
-      cand_path<MB>(total, nsub, cap, lo, nc, lk, row, region, score_stride, chunks, prefix_s, lds_key,
+      cand_path<MB>(total, nsub, cap, lo, nc, lk, row, region, score_stride, chunk, chunks, prefix_s, lds_key,
                 lds_cap, hist, sh);
     }
     if (direct) return;
