@@ -157,7 +157,7 @@ cs_status sparse_decode_attn_noalloc(const cs_decode_shape* shape, const void* q
  * sparse_decode_attn over the lists it selects (the end-to-end step whose indexer overhead the
  * technical summary, section 3.C, counts against the sparse kernel's gain).  Same arguments and
  * results as those two calls; `indices` (device int32 [B, T, Hq, k_max]) may be NULL when the
- * lists themselves are not wanted.  For k_max <= max_len / 16 (and max_len > 1024) each row's
+ * lists themselves are not wanted.  For k_max <= max_len / 8 (and max_len > 1024) each row's
  * selection and its attention run in one workgroup on the scores the indexer already computed;
  * otherwise the indexer (its full-score pass, or for max_len <= 1024 the whole-row pass that
  * scores every position and selects) leaves every score in the workspace and a further kernel

@@ -145,18 +145,17 @@ int64_t score_stride(const cs_decode_shape* s, const cs_kv_desc* kv, bool sketch
   return dense > cand ? dense : cand;
 }
 
-// The candidate pass addresses the rows of one (request, KV head) through a buffer resource,
-// whose size field is 32-bit: their score areas must span less than 2 GiB.
-// The candidate selection holds about 4.5 k candidates of a row in LDS: 12288 keys, or 24576 when
-// there are no more rows than compute units (one workgroup per unit); rows with more use its
-// global-memory path.  When even half of such lists would not fit (k_max sizes the lists, the
-// rows of a ragged batch mostly ask for fewer), the full-score path is used instead.
-int64_t cand_lds_keys(const cs_decode_shape* s) { return rows_of(s) <= cu_count() ? 24576 : 12288; }
-
+// The filtered indexer takes lists of at most 1/8 of the cache: at that bound the candidate
+// threshold keeps about 19% of a row's positions, well inside a slot's capacity (half of its
+// positions), and rows with more candidates than the selection's LDS key area select from the
+// slots in global memory.  Against the full-score path on 16 requests x 131072 positions: k = N/20
+// indexer 1033 -> 915 us, one-call step 1219 -> 1028 us; k = N/10 1055 -> 1030 and 1367 -> 1304;
+// k = N/5 measured 8% slower, so it stays on the full-score path.  The candidate pass addresses the
+// rows of one (request, KV head) through a buffer resource, whose size field is 32-bit: their
+// score areas must span less than 2 GiB.
 bool topk_filtered(const cs_decode_shape* s, const cs_kv_desc* kv, int k_max) {
   const int64_t span = (int64_t)s->q_len * s->num_q_heads * score_stride(s, kv, false) * 4;
-  return (int64_t)k_max * 16 <= kv->max_len && (int64_t)k_max * 9 / 2 <= 2 * cand_lds_keys(s) &&
-         span < (1LL << 31);
+  return (int64_t)k_max * 8 <= kv->max_len && span < (1LL << 31);
 }
 
 // ---- reduced-byte indexer sizing
@@ -189,11 +188,13 @@ struct SketchWs {
   size_t scores, hist, counts, tau, q_codes, q_scales, list_pos, list_score, sel_pos, sel_score, total;
 };
 
-// Lists longer than 1/16 of the cache come from every sketch score (the candidate slots hold
-// about half of a chunk's positions), as do lists whose candidates would not fit in LDS.
-bool sketch_full(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
+// Lists (m * k entries) longer than 1/16 of the cache come from every sketch score; shorter ones
+// from the candidate path, whose selection reads the slots from global memory for rows with more
+// candidates than its LDS key area (m = 1 at k = N/20: 939 -> 874 us; lists of N/10 measured no
+// faster than from every sketch score).
+bool sketch_full(const cs_decode_shape*, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult) {
   const int64_t keep = (int64_t)cand_mult * k_max;
-  return keep * 16 > kv->max_len || keep * 9 / 2 > 2 * cand_lds_keys(s);
+  return keep * 16 > kv->max_len;
 }
 
 SketchWs sketch_ws_layout(const cs_decode_shape* s, const cs_kv_desc* kv, int32_t k_max, int32_t cand_mult,

@@ -571,7 +571,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 // ============================================================================ filtered indexer
 // Writing every fp32 score and reading it back costs more than the 4 or 16 bytes per position
-// suggest (the writes interleave with the K stream), so for k <= N/16 the indexer avoids them:
+// suggest (the writes interleave with the K stream), so for k <= N/8 the indexer avoids them:
 //  A. sample_tau_kernel scores a strided sample of at most kTauSamples positions per (request,
 //     KV head) and sets, per row, a threshold tau: the 16-bit key prefix of the sample's r-th
 //     largest score, r from cand_rank (about 2.5 k samples / visible at 50x sparsity);
@@ -1705,7 +1705,7 @@ __global__ __launch_bounds__(kCsThreads) void cand_select_kernel(
   }
 }
 
-// The decode step on the full-score path (k > N/16): each row's index list (from select_kernel,
+// The decode step on the full-score path (k > N/8): each row's index list (from select_kernel,
 // ascending) with the scores score_hist_kernel already wrote for every visible position, so the
 // attention gathers V rows only.  One workgroup per row.
 template <int D, bool PAGED>

@@ -230,7 +230,7 @@ def test_ragged_paged_b32_t4():
 # 64 query rows per KV head, the largest page size, head_dim 64 at a long context
 
 def test_max_len_limit_filtered():
-    """262144 positions, k = N/50: the candidate path (k * 16 <= N)."""
+    """262144 positions, k = N/50: the candidate path (k * 8 <= N)."""
     from workloads import make_workload
 
     wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[262144],
@@ -239,11 +239,11 @@ def test_max_len_limit_filtered():
 
 
 def test_max_len_limit_full_score():
-    """262144 positions, k = N/8: the full-score path (every score, histogram select)."""
+    """262144 positions, k > N/8: the full-score path (every score, histogram select)."""
     from workloads import make_workload
 
     wl = make_workload(batch=1, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=128, seq_lens=[262144],
-                       k=32768, needles_per_head=2, seed=42, device="cuda")
+                       k=40000, needles_per_head=2, seed=42, device="cuda")
     _run(wl, seed=42)
 
 

@@ -70,7 +70,7 @@ def test_step_graph_replays_match_eager(layout):
 
 
 def test_every_entry_point_graph_replays_match_eager():
-    """topk_index on both paths (k <= N/16 and larger), sparse attention with splits (partials and
+    """topk_index on both paths (k <= N/8 and larger), sparse attention with splits (partials and
     the combine pass), dense attention, both sketch indexers and the full-score one-call step,
     captured together and replayed with eager work between replays."""
     m = _lib()
@@ -78,7 +78,7 @@ def test_every_entry_point_graph_replays_match_eager():
                        seq_lens=[9000, 4000], k=200, layout="paged", page_size=32, max_len=9216,
                        needles_per_head=2, seed=82).to("cuda")
     cache = cache_of(wl)
-    k_small, k_big = 200, 1500  # 200 * 16 <= 9216 < 1500 * 16
+    k_small, k_big = 200, 1500  # 200 * 8 <= 9216 < 1500 * 8
     kt_small = torch.full((wl.batch,), k_small, dtype=torch.int32, device="cuda")
     kt_big = torch.full((wl.batch,), k_big, dtype=torch.int32, device="cuda")
     sketch = m.key_sketch_build(cache)

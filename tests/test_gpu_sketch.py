@@ -195,9 +195,10 @@ def test_sketch_llama3_8b_n32k_k655_sampled_rows():
 
 
 def test_sketch_long_lists_large_capacity_select():
-    # 2 * k = 3000 of 65536 on 8 rows: the selection variant holding up to 24576 candidates
+    # 2 * k = 7000 of 131072 on 8 rows (candidate path, m * k <= N / 16): about 12900 candidates
+    # per row expected, so the selection variant holding up to 24576 of them in LDS
     wl = make_workload(batch=1, q_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
-                       seq_lens=[65536], k=1500, seed=72)
+                       seq_lens=[131072], k=3500, seed=72)
     _run(wl, m=2, step=True)
 
 

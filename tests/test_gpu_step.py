@@ -1,5 +1,5 @@
 """GPU parity of the one-call decode step (sparse_decode_step): the indexer and the sparse
-attention together, fused per row when k <= max_len / 16.
+attention together, fused per row when k <= max_len / 8.
 
 Each row is checked against the CPU oracle twice: its index list by the indexer's band rule, and
 (out, lse) against the oracle's sparse attention over that same list -- a set that differs from
@@ -82,7 +82,7 @@ def test_step_per_request_k_zero_and_all():
 
 
 def test_step_full_score_path():
-    # k > max_len / 16: indexer and attention run back to back
+    # k > max_len / 8: indexer and attention run back to back
     wl = make_workload(batch=2, q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=128,
                        seq_lens=[4096, 3000], k=600, max_len=4096, seed=55)
     _check_step(wl)
