@@ -1981,6 +1981,8 @@ static hipError_t launch_full_select_t(const TopkLaunch& a, int mult, int out_st
 // full-score path instead when a.sketch_full is set.
 template <int D, bool PAGED, bool SK>
 static hipError_t launch_filtered_t(const TopkLaunch& a, hipStream_t stream) {
+  // candidate positions are stored as 16-bit offsets within a wave's slot
+  if (a.cand_chunk / kCandWaves > 65536) return hipErrorInvalidValue;
   const int tiles = (a.GT + 15) / 16;
   const int groups = a.B * a.kv.num_kv_heads;
   hipError_t e;
